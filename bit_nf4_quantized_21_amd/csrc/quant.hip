@@ -1,0 +1,185 @@
+// Blockwise NF4 quantization, double quantization and dequantization kernels
+// for gfx950.
+//
+// NF4 and double quantization are items (a) and (b) of the QLoRA abstract
+// ("QLoRA: Efficient Finetuning of Quantized LLMs"); the block sizes (64 and
+// 256), the 8-bit constant format and the low-nibble-first packing are the
+// readings documented in include/qlora.h.
+//
+// All three kernels are HBM-bound streams.  The quantizer gives each 64-weight
+// block to 16 lanes (one 16-byte load per lane, a 4-step shuffle max for the
+// absmax) and decides every code exactly with fp64 products against the fp64
+// midpoints of the codebook; the double quantizer gives each group of 256
+// constants to one wavefront.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qlora {
+
+// ---------------------------------------------------------------------------
+// Quantize: W[n] fp32 -> codes[n/2], absmax[ceil(n/64)].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nf4_code(float w, double a64, const double* thr) {
+  // code = #{j : w > absmax * m_j}; thr[j] = absmax * m_j is exact in fp64.
+  double w64 = (double)w;
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (w64 > thr[j]) ? 1u : 0u;
+  return a64 == 0.0 ? 7u : c;
+}
+
+__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax, Midpoints mp) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (blk >= nb) return;  // whole 16-lane groups leave together
+  const int64_t e0 = blk * kBlock + l16 * 4;
+  const bool full = blk * kBlock + kBlock <= n;
+  float v[4];
+  if (full) {
+    float4 x = *reinterpret_cast<const float4*>(W + e0);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+  }
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+  for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+  if (l16 == 0) absmax[blk] = a;
+
+  const double a64 = (double)a;
+  double thr[15];
+#pragma unroll
+  for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
+  uint32_t c0 = nf4_code(v[0], a64, thr), c1 = nf4_code(v[1], a64, thr);
+  uint32_t c2 = nf4_code(v[2], a64, thr), c3 = nf4_code(v[3], a64, thr);
+  uint32_t packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
+  if (full) {
+    *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
+  } else {
+    if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);        // n is even: pairs are whole
+    if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Double quant: absmax[nb] -> q8[nb], s2[ceil(nb/256)].  One wave per group.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t q8_code(float c, double s2d, double scale) {
+  // Nearest integer to 255*c/s2, ties to even.  k0 = floor(c*255/s2) is
+  // within one of the answer; 510*c and (2*k0+1)*s2 are exact in fp64 and
+  // decide between k0 and k0+1.
+  double cd = (double)c;
+  double k0 = floor(cd * scale);
+  double lhs = 510.0 * cd, rhs = (2.0 * k0 + 1.0) * s2d;
+  int64_t k = (int64_t)k0;
+  if (lhs > rhs || (lhs == rhs && (k & 1))) k += 1;
+  k = k < 0 ? 0 : (k > 255 ? 255 : k);
+  return (uint32_t)k;
+}
+
+__global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax, int64_t nb,
+                                                           uint8_t* __restrict__ q8, float* __restrict__ s2) {
+  const int64_t ng = (nb + kBlock2 - 1) / kBlock2;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= ng) return;  // whole waves leave together
+  const int64_t e0 = g * kBlock2 + lane * 4;
+  const bool full = e0 + 4 <= nb;
+  float v[4];
+  if (full) {
+    float4 x = *reinterpret_cast<const float4*>(absmax + e0);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (e0 + i < nb) ? absmax[e0 + i] : 0.0f;
+  }
+  float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+#pragma unroll
+  for (int off = 32; off; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) s2[g] = m;
+  const double s2d = (double)m;
+  const double scale = m > 0.0f ? 255.0 / s2d : 0.0;
+  uint32_t q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = m > 0.0f ? q8_code(v[i], s2d, scale) : 0u;
+  if (full) {
+    *reinterpret_cast<uint32_t*>(q8 + e0) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e0 + i < nb) q8[e0 + i] = (uint8_t)q[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize (support): 8 weights per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ q8,
+                                                         const float* __restrict__ s2, int64_t n,
+                                                         int out_bf16, void* __restrict__ out, Codebook cb) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = cb.c[threadIdx.x];
+  __syncthreads();
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= n) return;
+  const int64_t b = e0 / kBlock;
+  const float sc = dq_scale(q8[b], s2[b / kBlock2]);
+  float w[8];
+  if (e0 + 8 <= n) {
+    uint32_t x = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = lut[(x >> (4 * i)) & 15] * sc;
+    if (out_bf16) {
+      u32x4 o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                 pack_bf16x2(w[6], w[7])};
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e0) = o;
+    } else {
+      float* o = reinterpret_cast<float*>(out) + e0;
+      *reinterpret_cast<float4*>(o) = make_float4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(w[4], w[5], w[6], w[7]);
+    }
+  } else {
+    for (int64_t e = e0; e < n; e += 2) {
+      uint32_t x = codes[e / 2];
+      float lo = lut[x & 15] * sc, hi = lut[x >> 4] * sc;
+      if (out_bf16) {
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + e) = pack_bf16x2(lo, hi);
+      } else {
+        reinterpret_cast<float*>(out)[e] = lo;
+        reinterpret_cast<float*>(out)[e + 1] = hi;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax,
+                               const Midpoints& mp, hipStream_t s) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t grid = (nb + 15) / 16;
+  hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* q8, float* s2, hipStream_t s) {
+  const int64_t ng = (nb + kBlock2 - 1) / kBlock2;
+  const int64_t grid = (ng + 3) / 4;
+  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, absmax, nb, q8, s2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
+                             int out_bf16, void* out, const Codebook& cb, hipStream_t s) {
+  const int64_t groups = (n + 7) / 8;
+  const int64_t grid = (groups + 255) / 256;
+  hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, codes, q8, s2, n, out_bf16,
+                     out, cb);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, its codebook equals the oracle's bit for bit, and argument
+errors come back as the documented status codes before anything is
+enqueued (no GPU is touched by these tests)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_21_amd import qlora
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+OK, ENULL, ESHAPE, EALIGN, EUNSUP, EHIP, EWS = 0, -1, -2, -3, -4, -5, -6
+P = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x10004)    # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qlora.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qlora._SIGNATURES)
+
+
+def test_codebook_matches_oracle_bitwise():
+    lib_cb = np.array(qlora.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), nf4.codebook().view(np.uint32))
+
+
+def test_status_strings(L):
+    for rc in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, EHIP, EWS):
+        assert L.qlora_status_string(rc).startswith(b"QLORA_")
+    assert L.qlora_last_hip_error() == 0
+
+
+def test_quantize_argument_errors(L):
+    assert L.qlora_quantize_nf4(P, 128, 32, P, P, None) == EUNSUP
+    assert L.qlora_quantize_nf4(P, 127, 64, P, P, None) == ESHAPE
+    assert L.qlora_quantize_nf4(P, -2, 64, P, P, None) == ESHAPE
+    assert L.qlora_quantize_nf4(None, 128, 64, P, P, None) == ENULL
+    assert L.qlora_quantize_nf4(P, 128, 64, None, P, None) == ENULL
+    assert L.qlora_quantize_nf4(MIS, 128, 64, P, P, None) == EALIGN
+    assert L.qlora_quantize_nf4(None, 0, 64, None, None, None) == OK   # empty input: no-op
+
+
+def test_double_quant_and_dequant_argument_errors(L):
+    assert L.qlora_double_quant(P, 10, 128, P, P, None) == EUNSUP
+    assert L.qlora_double_quant(P, -1, 256, P, P, None) == ESHAPE
+    assert L.qlora_double_quant(P, 10, 256, None, P, None) == ENULL
+    assert L.qlora_double_quant(P, 10, 256, P, MIS, None) == EALIGN
+    assert L.qlora_double_quant(None, 0, 256, None, None, None) == OK
+    assert L.qlora_dequantize_nf4(P, P, P, 3, 1, P, None) == ESHAPE
+    assert L.qlora_dequantize_nf4(P, P, P, 64, 2, P, None) == EUNSUP
+    assert L.qlora_dequantize_nf4(P, None, P, 64, 1, P, None) == ENULL
+    assert L.qlora_dequantize_nf4(P, P, P, 64, 1, MIS, None) == EALIGN
+
+
+def _fwd(L, T=4, K=128, N=64, r=8, X=P, Y=P, ws=P, wsb=1 << 30):
+    return L.qlora_linear_fwd(X, T, K, N, P, P, P, P, P, r, 16.0, Y, P, ws, wsb, None)
+
+
+def test_linear_fwd_argument_errors(L):
+    assert _fwd(L, K=96) == ESHAPE            # K % 64
+    assert _fwd(L, K=0) == ESHAPE
+    assert _fwd(L, N=12) == ESHAPE            # N % 8
+    assert _fwd(L, T=-1) == ESHAPE
+    assert _fwd(L, r=4) == EUNSUP
+    assert _fwd(L, r=136) == EUNSUP
+    assert _fwd(L, r=12) == EUNSUP
+    assert _fwd(L, X=None) == ENULL
+    assert _fwd(L, Y=MIS) == EALIGN
+    assert _fwd(L, T=0, X=None, Y=None) == OK  # no tokens: nothing to do
+    need = L.qlora_linear_fwd_workspace_bytes(4096, 4096, 4096, 64)
+    if need:
+        assert _fwd(L, T=4096, K=4096, N=4096, r=64, wsb=need - 1) == EWS
+        assert _fwd(L, T=4096, K=4096, N=4096, r=64, ws=None, wsb=need) == EWS
+    assert L.qlora_linear_fwd_workspace_bytes(4, 96, 64, 8) == 0   # invalid shape -> 0
+
+
+def test_linear_bwd_argument_errors(L):
+    def bwd(T=4, K=128, N=64, r=8, dX=P, dA=P, ws=P, wsb=1 << 30):
+        return L.qlora_linear_bwd(P, P, P, T, K, N, P, P, P, P, P, r, 16.0, dX, dA, P, ws, wsb, None)
+    assert bwd(K=100) == ESHAPE
+    assert bwd(r=0) == EUNSUP
+    assert bwd(dA=None) == ENULL
+    assert bwd(dX=None) == ENULL
+    assert bwd(dX=MIS) == EALIGN
+    need = L.qlora_linear_bwd_workspace_bytes(2048, 4096, 11008, 64)
+    if need:
+        assert bwd(T=2048, K=4096, N=11008, r=64, wsb=need - 1) == EWS
