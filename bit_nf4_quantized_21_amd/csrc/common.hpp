@@ -45,4 +45,53 @@ __device__ __forceinline__ float dq_scale(uint32_t q8, float s2) {
   return (float)((double)q8 * (double)s2 * (1.0 / 255.0));
 }
 
+// Decode 8 NF4 codes (one dword; element 2i in the low nibble of byte i) with
+// the per-block scale into 8 bf16 weights, packed as 4 bf16 pairs: the
+// compute weight bf16(c[code] * scale) of the dequantization rule.  `lut` is
+// the 16-entry fp32 codebook in LDS (16 distinct banks: conflict-free).
+__device__ __forceinline__ void decode8_bf16(uint32_t x, float sc, const float* lut, uint32_t out[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t b = x >> (8 * p);
+    out[p] = pack_bf16x2(lut[b & 15u] * sc, lut[(b >> 4) & 15u] * sc);
+  }
+}
+
+// Same decode to fp32 values (one fp32 multiply each, before bf16 rounding).
+__device__ __forceinline__ void decode8_f32(uint32_t x, float sc, const float* lut, float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = lut[(x >> (4 * e)) & 15u] * sc;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Split fp32 values into bf16 hi + lo parts (v ~= hi + lo to ~16 bits) so that
+// two bf16 MFMAs reproduce an fp32 operand to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16x8(const float v[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+    l[p] = pack_bf16x2(v[2 * p] - bf16_lo(h[p]), v[2 * p + 1] - bf16_hi(h[p]));
+  }
+  hi = as_bf16x8(h[0], h[1], h[2], h[3]);
+  lo = as_bf16x8(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float v[8]) {
+  return as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7]));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 }  // namespace qlora

@@ -1,0 +1,43 @@
+// Launchers of the dequantize-GEMM / GEMV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace qlora {
+
+struct FwdGemmParams {
+  const uint16_t* X;     // [T,K] bf16
+  const uint8_t* codes;  // [N*K/2]
+  const uint8_t* q8;     // [N*K/64]
+  const float* s2;       // [ceil(N*K/64/256)]
+  const uint16_t* B;     // [r,N] bf16
+  const float* XA;       // [T,r] fp32
+  uint16_t* Y;           // [T,N] bf16
+  int64_t T, K, N;
+  int r;
+  float s;
+  int tiles_n, tiles_m, per_xcd;  // filled by the launcher
+};
+
+struct DxGemmParams {
+  const uint16_t* dY;    // [T,N] bf16
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* A;     // [K,r] bf16
+  const float* G;        // [T,r] fp32
+  uint16_t* dX;          // [T,K] bf16
+  int64_t T, K, N;
+  int r;
+  float s;
+  int tiles_k, tiles_t, per_xcd;
+};
+
+hipError_t launch_gemm_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
+hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
+hipError_t launch_gemm_dx(const DxGemmParams& p, const Codebook& cb, hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,183 @@
+"""GPU parity of the forward and backward pass with the fp64 oracle.
+
+Bar: bit-exact NF4 codes and constants; for bf16 outputs and gradients a
+relative Frobenius error <= 5e-3 and an elementwise error <= 1e-2 of the
+output RMS (plus half a bf16 ulp, reading R10).  XA (fp32 output) must match
+to fp32 accumulation accuracy.  Inputs come from the seeded generator; the
+oracle quantizes W itself.  At full layer sizes, Y and dX are checked on
+sampled token rows (rows are independent) and dA, dB in full.
+"""
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_21_amd import synth
+from oracle import compare, lora, nf4
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _q():
+    from bit_nf4_quantized_21_amd import qlora
+    return qlora
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _f32(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+class Case:
+    def __init__(self, N, K, T, r, alpha=16.0, seed=0):
+        self.N, self.K, self.T, self.r, self.alpha = N, K, T, r, alpha
+        self.W = synth.weight(N, K, seed)
+        self.Xb = synth.x_bits(T, K, seed)
+        self.Ab = synth.a_bits(K, r, seed)
+        self.Bb = synth.b_bits(r, N, seed)
+        self.dYb = synth.dy_bits(T, N, seed)
+        self.X = nf4.bf16_bits_to_f32(self.Xb)
+        self.A = nf4.bf16_bits_to_f32(self.Ab)
+        self.B = nf4.bf16_bits_to_f32(self.Bb)
+        self.dY = nf4.bf16_bits_to_f32(self.dYb)
+
+    def oracle_weight(self):
+        codes, q8, s2, _ = nf4.quantize_all(self.W)
+        Wd = nf4.dequantize(codes, q8, s2, self.N * self.K, "bf16").reshape(self.N, self.K)
+        return codes, q8, s2, Wd
+
+    def gpu(self, bwd=True):
+        q = _q()
+        Wg = torch.from_numpy(self.W.ravel()).cuda()
+        codes, absmax = q.quantize_nf4(Wg)
+        q8, s2 = q.double_quant(absmax)
+        del Wg
+        Xg, Ag, Bg = _bf16_dev(self.Xb), _bf16_dev(self.Ab), _bf16_dev(self.Bb)
+        Y, XA = q.linear_fwd(Xg, codes, q8, s2, Ag, Bg, self.alpha, self.N)
+        out = {"codes": codes, "q8": q8, "s2": s2, "Y": Y, "XA": XA}
+        if bwd:
+            dYg = _bf16_dev(self.dYb)
+            dX, dA, dB = q.linear_bwd(dYg, Xg, XA, codes, q8, s2, Ag, Bg, self.alpha)
+            out.update(dX=dX, dA=dA, dB=dB)
+        torch.cuda.synchronize()
+        return out
+
+
+def _assert_close(name, got, ref):
+    ok, info = compare.check_close(got, ref)
+    assert ok, f"{name}: {info}"
+
+
+def _check(case, out, rows=None, bwd=True):
+    codes, q8, s2, Wd = case.oracle_weight()
+    assert np.array_equal(out["codes"].cpu().numpy(), codes)
+    assert np.array_equal(out["q8"].cpu().numpy(), q8)
+    assert np.array_equal(out["s2"].cpu().numpy(), s2)
+    rows = np.arange(case.T) if rows is None else rows
+    Yref, XAref = lora.linear_fwd(case.X[rows], Wd, case.A, case.B, case.alpha, case.r)
+    _assert_close("Y", _f32(out["Y"])[rows], Yref)
+    XA = out["XA"].cpu().numpy().astype(np.float64)[rows]
+    assert compare.rel_fro(XA, XAref) < 1e-5
+    if not bwd:
+        return
+    dXref = lora.dx_rows(case.dY[rows], Wd, case.A, case.B, case.alpha, case.r)
+    _assert_close("dX", _f32(out["dX"])[rows], dXref)
+    _, dAref, dBref, _ = lora.linear_bwd(case.dY, case.X, Wd, case.A, case.B, case.alpha, case.r)
+    _assert_close("dA", _f32(out["dA"]), dAref)
+    _assert_close("dB", _f32(out["dB"]), dBref)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_gemv_path_small_tokens(T):
+    print(f"gemv T={T}", flush=True)
+    c = Case(512, 512, T, 8, seed=10 + T)
+    _check(c, c.gpu())
+
+
+def test_tiny_config_fwd_bwd():
+    """W 512x512, X 32x512, r=8, alpha=16: the small workload in full."""
+    print("tiny", flush=True)
+    c = Case(512, 512, 32, 8, seed=0)
+    _check(c, c.gpu())
+
+
+@pytest.mark.parametrize("N,K,T,r", [(520, 576, 17, 16), (776, 640, 257, 64), (264, 1088, 300, 24),
+                                     (1024, 512, 513, 128)])
+def test_gemm_path_ragged(N, K, T, r):
+    """Several tiles in every dimension with ragged tails (N not a multiple of
+    256, K % 128 == 64, T not a multiple of 256), several ranks."""
+    print(f"ragged N={N} K={K} T={T} r={r}", flush=True)
+    c = Case(N, K, T, r, seed=N + K + T)
+    _check(c, c.gpu())
+
+
+def test_gemv_config_llama7b_qproj():
+    """4096x4096 q_proj, T=4, r=64: the HBM-bound small-token path in full."""
+    print("gemv 7B q_proj", flush=True)
+    c = Case(4096, 4096, 4, 64, seed=1)
+    _check(c, c.gpu(bwd=False), bwd=False)
+
+
+@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008)])
+def test_llama7b_mlp_full_size_sampled(N, K):
+    """7B MLP linears at T=2048: Y and dX on 48 sampled rows, dA and dB in full."""
+    print(f"7B MLP N={N} K={K}", flush=True)
+    c = Case(N, K, 2048, 64, seed=N)
+    out = c.gpu()
+    rows = np.random.Generator(np.random.PCG64(7)).choice(2048, 48, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, 2047]]))
+    _check(c, out, rows=rows)
+
+
+def test_zero_adapter_and_zero_weight():
+    """B = 0 leaves the base output and gives dA = 0; W = 0 isolates the adapter."""
+    c = Case(256, 256, 40, 8, seed=3)
+    c.Bb = np.zeros_like(c.Bb)
+    c.B = nf4.bf16_bits_to_f32(c.Bb)
+    out = c.gpu()
+    _check(c, out)
+    assert torch.count_nonzero(out["dA"]).item() == 0
+    c2 = Case(256, 256, 40, 8, seed=4)
+    c2.W = np.zeros_like(c2.W)
+    _check(c2, c2.gpu())
+
+
+def test_deterministic():
+    c = Case(776, 640, 300, 64, seed=5)
+    a, b = c.gpu(), c.gpu()
+    for k in ("Y", "XA", "dX", "dA", "dB"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_no_tokens_backward_zeroes_adapter_grads():
+    q = _q()
+    K, N, r = 128, 64, 8
+    dA = torch.full((K, r), 3.0, dtype=torch.bfloat16, device="cuda")
+    dB = torch.full((r, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros(N * K // 2, dtype=torch.uint8, device="cuda")
+    q8 = torch.zeros(N * K // 64, dtype=torch.uint8, device="cuda")
+    s2 = torch.zeros((N * K // 64 + 255) // 256, dtype=torch.float32, device="cuda")
+    X = torch.empty(0, K, dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty(0, N, dtype=torch.bfloat16, device="cuda")
+    XA = torch.empty(0, r, dtype=torch.float32, device="cuda")
+    A = torch.zeros(K, r, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(r, N, dtype=torch.bfloat16, device="cuda")
+    q.linear_bwd(dY, X, XA, codes, q8, s2, A, B, 16.0, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA).item() == 0 and torch.count_nonzero(dB).item() == 0
+
+
+def test_argument_errors_raise():
+    q = _q()
+    X = torch.zeros(4, 96, dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros(64 * 96 // 2, dtype=torch.uint8, device="cuda")
+    q8 = torch.zeros(96, dtype=torch.uint8, device="cuda")
+    s2 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    A = torch.zeros(96, 8, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(q.QLoRAError):
+        q.linear_fwd(X, codes, q8, s2, A, B, 16.0, 64)   # K = 96 is not a multiple of 64
