@@ -94,4 +94,35 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer descriptors: loads at offsets at or past `bytes` return zero, so
+// ragged tile edges need no branches.  Offsets are 32-bit, relative to base.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// Asynchronous copy of 16 bytes per lane from a buffer straight into LDS
+// (buffer_load_dwordx4 ... lds): lane i of the wave writes the 16 bytes at
+// byte offset `off` of the buffer to lds_block + 16 * i.  Completion is
+// tracked by vmcnt like any buffer load.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void buf_load16_to_lds(rsrc_t r, void* lds_block, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_block, 16, (int)off, 0, 0, 0);
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only (global
+// loads stay in flight across it).  The memory clobber keeps the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace qlora

@@ -20,6 +20,7 @@
 //  * Double-buffered: the next step's codes and dY are loaded during the
 //    MFMAs of the current step and decoded / stored after them.
 #include "common.hpp"
+#include "timing.hpp"
 #include "gemm.hpp"
 
 namespace qlora {
@@ -206,7 +207,10 @@ hipError_t launch_gemm_dx(const DxGemmParams& p0, const Codebook& cb, hipStream_
   p.tiles_t = (int)((p.T + kTileT - 1) / kTileT);
   const int total = p.tiles_k * p.tiles_t;
   p.per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(gemm_dx_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+  {
+    KernelTimer kt_("gemm_dx_kernel", s);
+    hipLaunchKernelGGL(gemm_dx_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+  }
   return hipGetLastError();
 }
 

@@ -8,41 +8,63 @@
 // example: NF4, double quantization, bf16 compute); the second term is the
 // adapter's s (X A) B (LoRA tutorial, h = W x + dW x, with alpha/r scaling).
 //
-// Design (one workgroup = 4 waves = a 256 (n) x 256 (m) output tile):
+// Design (one workgroup = 4 waves, one per SIMD = a 256 (n) x 256 (m) tile):
 //  * K advances one 64-weight quant block per step, so each W row contributes
-//    exactly one 32-byte code segment and one scale per step.
-//  * W' never touches LDS: lane (row, half) loads its 16 code bytes and
-//    decodes them straight into the MFMA A-operand registers.  Each W row is
-//    decoded once per workgroup (waves partition n), so the dequant cost is
-//    amortised over 256 tokens.
-//  * The contraction order inside a step is a fixed permutation of k: lane
-//    half h, substep s, element i covers k = 32h + 8s + i.  X is read from
+//    one 32-byte code segment and one scale per step.
+//  * W' never touches LDS: lane (row, half h) loads its 16 code bytes and
+//    decodes them straight into the MFMA A-operand registers.  Waves
+//    partition n, so each W row is decoded once per workgroup and the
+//    dequantization cost is amortised over 256 tokens.
+//  * Inside a step the contraction runs over a fixed permutation of k: lane
+//    half h, substep s, element i covers k = 32h + 8s + i; X is read from
 //    LDS in the same permuted order, so the sum is unchanged.
-//  * X tiles (256 x 64 bf16) are double-buffered in LDS with a 144-byte row
-//    pitch (16 consecutive rows hit 16 distinct 4-bank groups); the next
-//    step's X and the step after next's codes are in flight during the MFMAs.
-//  * Workgroup order is XCD-aware: tiles that share W rows are dispatched to
-//    the same XCD so the codes are fetched from HBM once per L2.
+//  * Software pipeline per step (4 substeps x 16 MFMAs): during substep s the
+//    X operands of substep s+1 are read from LDS, the codebook values of
+//    chunk s of the next step's W are fetched from the LDS table, and the
+//    values fetched one substep earlier are scaled and packed to bf16 -- all
+//    interleaved between the MFMAs (one wave can hide ~6 VALU issues under a
+//    32x32x16 MFMA).  X tiles stream into a 3-stage LDS ring by direct
+//    buffer-to-LDS loads issued three steps ahead (no registers, no LDS
+//    writes); codes are loaded two steps ahead into registers.  One barrier
+//    per step sits after substep 2, so the next step's first operand reads
+//    overlap substep 3.
+//  * X rows are 128 bytes in LDS with the 16-byte chunk index XOR-ed with
+//    bits 1..3 of the row: the 16 rows read by one 16-lane phase land in 16
+//    distinct 4-bank groups of gfx950's 64-bank LDS.
+//  * Ragged tiles use buffer loads, which return zero past the end.
+//  * Workgroup order is XCD-aware: each XCD works through a contiguous run of
+//    token-tile-major tiles, so an X tile is fetched into an XCD's L2 once and
+//    re-read from there by every n-tile.
 #include "common.hpp"
 #include "gemm.hpp"
+#include "timing.hpp"
 
 namespace qlora {
 
 namespace {
 constexpr int kTileN = 256;
 constexpr int kTileM = 256;
-constexpr int kXPitch = 72;  // bf16 per LDS row (64 + 8)
+constexpr int kStageBytes = kTileM * 128;  // one X stage: 256 rows x 64 bf16
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  __shared__ __align__(16) uint16_t xs[2][kTileM * kXPitch];
+  // Separate LDS objects for the codebook and each ring stage: the compiler
+  // can then prove that operand reads of one stage never alias the
+  // buffer-to-LDS loads in flight into another, and inserts no waits for them.
   __shared__ float lut[16];
+  __shared__ __align__(1024) unsigned char xs0[kStageBytes];
+  __shared__ __align__(1024) unsigned char xs1[kStageBytes];
+  __shared__ __align__(1024) unsigned char xs2[kStageBytes];
+  unsigned char* const xring[3] = {xs0, xs1, xs2};
   const int tid = threadIdx.x;
 
+  // Workgroups are dispatched round-robin over the 8 XCDs; tiles are ordered
+  // token-tile-major and each XCD takes a contiguous run of them, so the X
+  // tile (the operand re-read by every n-tile) stays in that XCD's L2.
   const int bid = blockIdx.x;
   const int tile = (bid & 7) * p.per_xcd + (bid >> 3);
   if (tile >= p.tiles_n * p.tiles_m) return;  // uniform per workgroup, before any barrier
-  const int tn = tile / p.tiles_m, tm = tile % p.tiles_m;
+  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
 
   if (tid < 16) lut[tid] = cb.c[tid];
 
@@ -52,53 +74,64 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int64_t K2 = K / 2, bpr = K / 64;
   const int nk = (int)(K / 64);
 
-  int64_t nrow[2];
+  // Buffer views of this tile's rows: reads past the last row return zero.
+  const rsrc_t rx = make_rsrc(p.X + m0 * K, (T - m0) * K * 2);
+  const rsrc_t rc = make_rsrc(p.codes + n0 * K2, (N - n0) * K2);
+  const rsrc_t rq = make_rsrc(p.q8 + n0 * bpr, (N - n0) * bpr);
+  const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
+
+  int nl[2];
   bool nval[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    nrow[g] = n0 + 64 * wave + 32 * g + ml;
-    nval[g] = nrow[g] < N;
+    nl[g] = 64 * wave + 32 * g + ml;
+    nval[g] = n0 + nl[g] < N;
   }
-  const int xc = tid & 7, xr = tid >> 3;
 
-  auto load_x = [&](int kb, u32x4(&v)[8]) {
+  // Direct X loads: wave w fills rows [64w, 64w+64) of a stage, 8 rows per
+  // instruction; lane l covers row 8j + l/8 of its block, physical chunk l%8,
+  // which holds logical chunk (l%8) ^ ((row >> 1) & 7).
+  const int dr = lane >> 3, dpc = lane & 7;
+  const uint32_t xoff_even = (uint32_t)(dr * K * 2 + ((dpc ^ (dr >> 1)) << 4));
+  const uint32_t xoff_odd = (uint32_t)(dr * K * 2 + ((dpc ^ ((dr >> 1) | 4)) << 4));
+  auto dma_x = [&](int kb, int stage) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      v[i] = (m < T) ? *reinterpret_cast<const u32x4*>(p.X + m * K + (int64_t)kb * 64 + xc * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 8; ++j) {
+      const int row0 = 64 * wave + 8 * j;
+      buf_load16_to_lds(rx, xring[stage] + row0 * 128,
+                        ((j & 1) ? xoff_odd : xoff_even) + (uint32_t)(row0 * K * 2 + kb * 128));
     }
-  };
-  auto store_x = [&](int buf, const u32x4(&v)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&xs[buf][(xr + 32 * i) * kXPitch + xc * 8]) = v[i];
   };
   auto load_w = [&](int kb, u32x4(&c)[2], uint32_t(&q)[2], float(&sv)[2]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      if (nval[g]) {
-        c[g] = *reinterpret_cast<const u32x4*>(p.codes + nrow[g] * K2 + (int64_t)kb * 32 + 16 * h);
-        const int64_t b = nrow[g] * bpr + kb;
-        q[g] = p.q8[b];
-        sv[g] = p.s2[b >> 8];
-      } else {
-        c[g] = u32x4{0u, 0u, 0u, 0u};
-        q[g] = 0u;
-        sv[g] = 0.0f;
-      }
+      c[g] = buf_load16(rc, (uint32_t)(nl[g] * K2 + kb * 32 + 16 * h));
+      q[g] = buf_load1(rq, (uint32_t)(nl[g] * bpr + kb));
+      const int64_t b = (n0 + nl[g]) * bpr + kb;
+      sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
     }
   };
-  auto decode = [&](const u32x4(&c)[2], const uint32_t(&q)[2], const float(&sv)[2], bf16x8(&w)[2][4]) {
+  // Codebook lookups for 8 codes: the byte offset of each code's table entry
+  // is a byte of (x << 2) or (x >> 2).
+  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  auto lut8 = [&](uint32_t x, float(&f)[8]) {
+    const uint32_t y4 = (x << 2) & 0x3C3C3C3Cu, z4 = (x >> 2) & 0x3C3C3C3Cu;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float sc = dq_scale(q[g], sv[g]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t o[4];
-        decode8_bf16(c[g][s], sc, lut, o);
-        w[g][s] = as_bf16x8(o[0], o[1], o[2], o[3]);
-      }
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(y4, 8 * q, 8));
+      f[2 * q + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(z4, 8 * q, 8));
     }
+  };
+  auto pack8 = [&](const float(&f)[8], float sc) -> bf16x8 {
+    return as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                     pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc));
+  };
+  // B operand (X) of substep s: row 32 mi + ml, logical chunk 4h + s.
+  const int sw = (ml >> 1) & 7;
+  auto read_x = [&](int stage, int s, bf16x8(&xo)[8]) {
+    const unsigned char* b = xring[stage] + ml * 128 + (((4 * h + s) ^ sw) << 4);
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) xo[mi] = *reinterpret_cast<const bf16x8*>(b + mi * 4096);
   };
 
   f32x16 acc[2][8];
@@ -109,55 +142,102 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[g][mi][e] = 0.0f;
 
-  u32x4 xreg[8];
-  u32x4 creg[2];
-  uint32_t qreg[2];
-  float sreg[2];
-  bf16x8 wop[2][4];
+  u32x4 cA[2], cB[2];           // codes of the next step / the step after
+  uint32_t qA[2], qB[2];
+  float sA[2], sB[2];
+  bf16x8 wc[2][4], wn[2][3];    // W' operands of this step; chunks 0..2 of the next
+  float fp[2][8];               // codebook values of a chunk awaiting scale + pack
+  float scp[2];                 // the scales of the chunk pending in fp
+  bf16x8 xa[8], xb[8];          // X operands, alternating substeps
 
-  load_x(0, xreg);
-  load_w(0, creg, qreg, sreg);
-  __syncthreads();  // lut
-  store_x(0, xreg);
-  decode(creg, qreg, sreg, wop);
-  if (nk > 1) load_w(1, creg, qreg, sreg);
-  __syncthreads();
-
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < nk;
-    if (more) load_x(kb + 1, xreg);
-    u32x4 cn[2];
-    uint32_t qn[2];
-    float sn[2];
-    if (kb + 2 < nk) load_w(kb + 2, cn, qn, sn);
-
-    const uint16_t* xb = xs[buf];
+  // Prologue: X(0..2) into the ring, W(0) decoded, codes(1) in flight.
+  dma_x(0, 0);
+  dma_x(nk > 1 ? 1 : 0, 1);
+  dma_x(nk > 2 ? 2 : 0, 2);
+  load_w(0, cA, qA, sA);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // lut and X(0..2) visible to every wave
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 xop[8];
+  for (int g = 0; g < 2; ++g) {
+    const float sc = dq_scale(qA[g], sA[g]);
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-        xop[mi] = *reinterpret_cast<const bf16x8*>(&xb[(32 * mi + ml) * kXPitch + 32 * h + 8 * s]);
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) acc[g][mi] = mfma32(wop[g][s], xop[mi], acc[g][mi]);
+    for (int s = 0; s < 3; ++s) {
+      float f[8];
+      lut8(cA[g][s], f);
+      wc[g][s] = pack8(f, sc);
     }
-    if (more) {
-      decode(creg, qreg, sreg, wop);
-      store_x(buf ^ 1, xreg);
-    }
-    if (kb + 2 < nk) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        creg[g] = cn[g];
-        qreg[g] = qn[g];
-        sreg[g] = sn[g];
-      }
-    }
-    __syncthreads();
+    lut8(cA[g][3], fp[g]);  // chunk 3 of W(0) is packed in the first substep, like every step's
+    scp[g] = sc;
   }
+  load_w(nk > 1 ? 1 : 0, cA, qA, sA);
+  read_x(0, 0, xa);
+
+  // Substep S: MFMAs on (wc[.][S], XCUR); X of the next substep -> XNXT;
+  // PACK the chunk pending in fp; fetch the codebook values of chunk S of
+  // the next step (codes CA) into fp.
+#define QLORA_FWD_SUBSTEP(S, XCUR, XNXT, NXTSTAGE, NXTS, CA, PACK)                      \
+  {                                                                                     \
+    read_x(NXTSTAGE, NXTS, XNXT);                                                       \
+    PACK;                                                                               \
+    lut8(CA[0][S], fp[0]);                                                              \
+    lut8(CA[1][S], fp[1]);                                                              \
+    _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
+      acc[0][mi] = mfma32(wc[0][S], XCUR[mi], acc[0][mi]);                              \
+      acc[1][mi] = mfma32(wc[1][S], XCUR[mi], acc[1][mi]);                              \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
+    }                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  }
+
+  // One pipelined step on ring stage ST (the next step's stage is ST1).  CA..
+  // name the register set holding the codes of step kb+1 (decoded now), CB..
+  // the set that receives the codes of step kb+2.  The loop is unrolled by
+  // six so code sets (period 2) and stages (period 3) are compile-time
+  // constants: no register copies (a copy would wait for the load just
+  // issued) and statically distinct LDS objects.
+#define QLORA_FWD_STEP(KB, ST, ST1, CA, QA, SA, CB, QB, SB)                                            \
+  {                                                                                                    \
+    const int st = (ST), st1 = (ST1);                                                                  \
+    const int kn2 = (KB) + 2 < nk ? (KB) + 2 : nk - 1; /* past the end: redundant, in bounds */        \
+    const int kn3 = (KB) + 3 < nk ? (KB) + 3 : nk - 1;                                                 \
+    load_w(kn2, CB, QB, SB);                                                                           \
+    const float sc0 = dq_scale(QA[0], SA[0]), sc1 = dq_scale(QA[1], SA[1]);                             \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+    QLORA_FWD_SUBSTEP(0, xa, xb, st, 1, CA,                                                            \
+                      { wc[0][3] = pack8(fp[0], scp[0]); wc[1][3] = pack8(fp[1], scp[1]); })            \
+    QLORA_FWD_SUBSTEP(1, xb, xa, st, 2, CA, { wn[0][0] = pack8(fp[0], sc0); wn[1][0] = pack8(fp[1], sc1); }) \
+    QLORA_FWD_SUBSTEP(2, xa, xb, st, 3, CA, { wn[0][1] = pack8(fp[0], sc0); wn[1][1] = pack8(fp[1], sc1); }) \
+    /* X(kb+1) must be in LDS: of this wave's loads only the 8 X loads of   */                         \
+    /* step kb+2 and the 6 code loads of step kb+2 may still be in flight.  */                         \
+    /* After the barrier every wave is done with stage st, which the loads  */                         \
+    /* of X(kb+3) overwrite.                                                  */                       \
+    asm volatile("s_waitcnt vmcnt(14)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
+    dma_x(kn3, st);                                                                                    \
+    QLORA_FWD_SUBSTEP(3, xb, xa, st1, 0, CA,                                                           \
+                      { wn[0][2] = pack8(fp[0], sc0); wn[1][2] = pack8(fp[1], sc1); })                  \
+    scp[0] = sc0;                                                                                      \
+    scp[1] = sc1;                                                                                      \
+    _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                                    \
+      _Pragma("unroll") for (int s = 0; s < 3; ++s) wc[g][s] = wn[g][s];                              \
+    }                                                                                                  \
+  }
+
+  for (int kb = 0; kb < nk; kb += 6) {
+    QLORA_FWD_STEP(kb, 0, 1, cA, qA, sA, cB, qB, sB)
+    if (kb + 1 < nk) QLORA_FWD_STEP(kb + 1, 1, 2, cB, qB, sB, cA, qA, sA)
+    if (kb + 2 < nk) QLORA_FWD_STEP(kb + 2, 2, 0, cA, qA, sA, cB, qB, sB)
+    if (kb + 3 < nk) QLORA_FWD_STEP(kb + 3, 0, 1, cB, qB, sB, cA, qA, sA)
+    if (kb + 4 < nk) QLORA_FWD_STEP(kb + 4, 1, 2, cA, qA, sA, cB, qB, sB)
+    if (kb + 5 < nk) QLORA_FWD_STEP(kb + 5, 2, 0, cB, qB, sB, cA, qA, sA)
+  }
+#undef QLORA_FWD_STEP
+#undef QLORA_FWD_SUBSTEP
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load into LDS may outlive the kernel
+  __syncthreads();
 
   // LoRA up-projection as one extra K-step of width r: A = B^T (rows n),
   // B operand = s * XA (columns m) as a bf16 hi + lo pair, so the fp32 XA
@@ -171,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     for (int g = 0; g < 2; ++g) {
       uint32_t e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = (nval[g] && jv) ? p.B[(int64_t)(j0 + i) * N + nrow[g]] : 0u;
+      for (int i = 0; i < 8; ++i) e[i] = (nval[g] && jv) ? p.B[(int64_t)(j0 + i) * N + n0 + nl[g]] : 0u;
       aop[g] = as_bf16x8(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
     }
 #pragma unroll
@@ -223,7 +303,10 @@ hipError_t launch_gemm_fwd(const FwdGemmParams& p0, const Codebook& cb, hipStrea
   p.tiles_m = (int)((p.T + kTileM - 1) / kTileM);
   const int total = p.tiles_n * p.tiles_m;
   p.per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(gemm_fwd_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+  {
+    KernelTimer kt_("gemm_fwd_kernel", s);
+    hipLaunchKernelGGL(gemm_fwd_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+  }
   return hipGetLastError();
 }
 

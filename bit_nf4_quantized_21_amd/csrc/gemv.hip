@@ -15,6 +15,7 @@
 // are issued two chunks ahead of the decode so that a wave keeps ~8 KB of
 // HBM traffic in flight.
 #include "common.hpp"
+#include "timing.hpp"
 #include "gemm.hpp"
 
 namespace qlora {
@@ -115,7 +116,10 @@ __global__ __launch_bounds__(512) void gemv_fwd_kernel(FwdGemmParams p, Codebook
 
 hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s) {
   const unsigned grid = (unsigned)((p.N + kRowsPerWG - 1) / kRowsPerWG);
-  hipLaunchKernelGGL(gemv_fwd_kernel, dim3(grid), dim3(512), 0, s, p, cb);
+  {
+    KernelTimer kt_("gemv_fwd_kernel", s);
+    hipLaunchKernelGGL(gemv_fwd_kernel, dim3(grid), dim3(512), 0, s, p, cb);
+  }
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 // and G) enter the MFMA as a bf16 hi + lo pair, which keeps the adapter
 // gradients at ~16-bit operand precision.
 #include "common.hpp"
+#include "timing.hpp"
 #include "lora.hpp"
 
 namespace qlora {
@@ -176,12 +177,21 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_kmajor, fl
   const int64_t nc = (L + LC - 1) / LC;
   dim3 grid((unsigned)((T + 63) / 64), (unsigned)nc);
   if (v_kmajor)
-    hipLaunchKernelGGL(rowdot_partial_kernel<true>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+    {
+      KernelTimer kt_("rowdot_partial_kernel", s);
+      hipLaunchKernelGGL(rowdot_partial_kernel<true>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+    }
   else
-    hipLaunchKernelGGL(rowdot_partial_kernel<false>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+    {
+      KernelTimer kt_("rowdot_partial_kernel", s);
+      hipLaunchKernelGGL(rowdot_partial_kernel<false>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+    }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rowdot_reduce_kernel, dim3(blocks_for(T * r / 4)), dim3(256), 0, s, P, out, T, r, (int)nc);
+  {
+    KernelTimer kt_("rowdot_reduce_kernel", s);
+    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3(blocks_for(T * r / 4)), dim3(256), 0, s, P, out, T, r, (int)nc);
+  }
   return hipGetLastError();
 }
 
@@ -189,17 +199,26 @@ hipError_t launch_tokdot(const uint16_t* M, const float* S, float* P, uint16_t* 
                          int64_t TC, float scale, bool transpose, hipStream_t s) {
   const int64_t nc = (T + TC - 1) / TC;
   dim3 grid((unsigned)((C + 63) / 64), (unsigned)nc);
-  hipLaunchKernelGGL(tokdot_partial_kernel, grid, dim3(256), 0, s, M, S, P, T, C, r, TC);
+  {
+    KernelTimer kt_("tokdot_partial_kernel", s);
+    hipLaunchKernelGGL(tokdot_partial_kernel, grid, dim3(256), 0, s, M, S, P, T, C, r, TC);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tokdot_reduce_kernel, dim3(blocks_for(C * r / 4)), dim3(256), 0, s, P, out, C, r, (int)nc,
+  {
+    KernelTimer kt_("tokdot_reduce_kernel", s);
+    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3(blocks_for(C * r / 4)), dim3(256), 0, s, P, out, C, r, (int)nc,
                      scale, transpose ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_u16_kernel, dim3(blocks_for(n)), dim3(256), 0, s, p, n);
+  {
+    KernelTimer kt_("zero_u16_kernel", s);
+    hipLaunchKernelGGL(zero_u16_kernel, dim3(blocks_for(n)), dim3(256), 0, s, p, n);
+  }
   return hipGetLastError();
 }
 

@@ -5,11 +5,13 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <string>
 
 #include "../../include/qlora.h"
 #include "codebook.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace {
 
@@ -69,6 +71,20 @@ const char* qlora_status_string(int status) {
 }
 
 int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+void qlora_timing_enable(int on) { qlora::timing_enable(on != 0); }
+
+int qlora_timing_read(char* buf, size_t buflen) {
+  hipError_t e = hipSuccess;
+  const std::string text = qlora::timing_collect(&e);
+  if (buf && buflen) {
+    const size_t n = text.size() < buflen - 1 ? text.size() : buflen - 1;
+    std::memcpy(buf, text.data(), n);
+    buf[n] = '\0';
+  }
+  if (e != hipSuccess) return hip_status(e);
+  return (int)text.size();
+}
 
 int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize, uint8_t* codes, float* absmax,
                        void* stream) {

@@ -12,6 +12,7 @@
 // midpoints of the codebook; the double quantizer gives each group of 256
 // constants to one wavefront.
 #include "common.hpp"
+#include "timing.hpp"
 #include "kernels.hpp"
 
 namespace qlora {
@@ -162,14 +163,20 @@ hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float*
                                const Midpoints& mp, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t grid = (nb + 15) / 16;
-  hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+  {
+    KernelTimer kt_("quantize_nf4_kernel", s);
+    hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* q8, float* s2, hipStream_t s) {
   const int64_t ng = (nb + kBlock2 - 1) / kBlock2;
   const int64_t grid = (ng + 3) / 4;
-  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, absmax, nb, q8, s2);
+  {
+    KernelTimer kt_("double_quant_kernel", s);
+    hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, absmax, nb, q8, s2);
+  }
   return hipGetLastError();
 }
 
@@ -177,8 +184,11 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const floa
                              int out_bf16, void* out, const Codebook& cb, hipStream_t s) {
   const int64_t groups = (n + 7) / 8;
   const int64_t grid = (groups + 255) / 256;
-  hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, codes, q8, s2, n, out_bf16,
+  {
+    KernelTimer kt_("dequantize_kernel", s);
+    hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, codes, q8, s2, n, out_bf16,
                      out, cb);
+  }
   return hipGetLastError();
 }
 

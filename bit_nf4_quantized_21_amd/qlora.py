@@ -29,6 +29,8 @@ _SIGNATURES = {
                                         _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "qlora_linear_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                         _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "qlora_timing_enable": (None, [ctypes.c_int]),
+    "qlora_timing_read": (ctypes.c_int, [ctypes.c_char_p, _c_sz]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_last_hip_error": (ctypes.c_int, []),
@@ -88,6 +90,27 @@ def _stream(stream=None):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def timing_enable(on=True):
+    """Bracket every library kernel launch with HIP events (benchmarks only)."""
+    lib().qlora_timing_enable(1 if on else 0)
+
+
+def timing_read():
+    """{kernel_name: (launches, total_ms)} for the launches since the last read."""
+    size = 1 << 20
+    buf = ctypes.create_string_buffer(size)
+    rc = lib().qlora_timing_read(buf, size)   # collects and forgets in one call
+    if rc < 0:
+        _check(rc)
+    if rc >= size:
+        raise QLoRAError("timing report truncated")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        out[name] = (int(n), float(ms))
+    return out
 
 
 def nf4_codebook():

@@ -154,6 +154,18 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA,
 int qlora_dequantize_nf4(const uint8_t* codes, const uint8_t* q8, const float* s2,
                          int64_t n, int32_t out_is_bf16, void* out, void* stream);
 
+/*
+ * Support: per-kernel timing for benchmarks.  While enabled, every kernel the
+ * library enqueues is bracketed by two HIP events recorded on the stream it
+ * is launched on.  qlora_timing_read waits for those events, writes one line
+ * "kernel_name launches total_ms" per kernel (NUL-terminated, truncated to
+ * buflen) into the host buffer buf, forgets the records, and returns the
+ * length of the full text, or QLORA_ERR_HIP if an event query failed.
+ * Timing adds two event records per launch; leave it off otherwise.
+ */
+void qlora_timing_enable(int on);
+int qlora_timing_read(char* buf, size_t buflen);
+
 /* Host: copy the library's 16-entry fp32 NF4 codebook (ascending) to out. */
 void qlora_nf4_codebook(float out[16]);
 
