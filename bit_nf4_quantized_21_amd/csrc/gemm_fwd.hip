@@ -23,14 +23,18 @@
 //    chunk s of the next step's W are fetched from the LDS table, and the
 //    values fetched one substep earlier are scaled and packed to bf16 -- all
 //    interleaved between the MFMAs (one wave can hide ~6 VALU issues under a
-//    32x32x16 MFMA).  X tiles stream into a 3-stage LDS ring by direct
-//    buffer-to-LDS loads issued three steps ahead (no registers, no LDS
-//    writes); codes are loaded two steps ahead into registers.  One barrier
-//    per step sits after substep 2, so the next step's first operand reads
-//    overlap substep 3.
+//    32x32x16 MFMA).  X tiles go through a 3-stage LDS ring: each lane
+//    loads its 8 x 16 bytes of the tile two steps ahead into registers and
+//    writes them to LDS one step later, so every global load has a full step
+//    to arrive before anything waits on it.  Codes are loaded two steps
+//    ahead into registers.  One barrier per step sits after substep 2, so
+//    the next step's first operand reads overlap substep 3.
 //  * X rows are 128 bytes in LDS with the 16-byte chunk index XOR-ed with
 //    bits 1..3 of the row: the 16 rows read by one 16-lane phase land in 16
-//    distinct 4-bank groups of gfx950's 64-bank LDS.
+//    distinct 4-bank groups of gfx950's 64-bank LDS, and the 16 lanes of a
+//    write phase cover two adjacent rows, i.e. all 64 banks.
+//  * The codebook sits at LDS address 0, so a table lookup's address is one
+//    bitfield extract of the code byte.
 //  * Ragged tiles use buffer loads, which return zero past the end.
 //  * Workgroup order is XCD-aware: each XCD works through a contiguous run of
 //    token-tile-major tiles, so an X tile is fetched into an XCD's L2 once and
@@ -45,17 +49,15 @@ namespace {
 constexpr int kTileN = 256;
 constexpr int kTileM = 256;
 constexpr int kStageBytes = kTileM * 128;  // one X stage: 256 rows x 64 bf16
+constexpr int kLutBytes = 1024;            // codebook slot (keeps stages 1 KiB aligned)
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  // Separate LDS objects for the codebook and each ring stage: the compiler
-  // can then prove that operand reads of one stage never alias the
-  // buffer-to-LDS loads in flight into another, and inserts no waits for them.
-  __shared__ float lut[16];
-  __shared__ __align__(1024) unsigned char xs0[kStageBytes];
-  __shared__ __align__(1024) unsigned char xs1[kStageBytes];
-  __shared__ __align__(1024) unsigned char xs2[kStageBytes];
-  unsigned char* const xring[3] = {xs0, xs1, xs2};
+  // LDS: the codebook at address 0, then the three X stages.
+  __shared__ __align__(1024) unsigned char smem[kLutBytes + 3 * kStageBytes];
+  float* const lut = reinterpret_cast<float*>(smem);
+  unsigned char* const xring[3] = {smem + kLutBytes, smem + kLutBytes + kStageBytes,
+                                   smem + kLutBytes + 2 * kStageBytes};
   const int tid = threadIdx.x;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tiles are ordered
@@ -88,19 +90,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     nval[g] = n0 + nl[g] < N;
   }
 
-  // Direct X loads: wave w fills rows [64w, 64w+64) of a stage, 8 rows per
-  // instruction; lane l covers row 8j + l/8 of its block, physical chunk l%8,
-  // which holds logical chunk (l%8) ^ ((row >> 1) & 7).
+  // X staging: wave w moves rows [64w, 64w+64) of a stage, 8 rows per
+  // instruction; lane l covers row 64w + 8j + l/8, logical chunk l%8, stored
+  // at physical chunk (l%8) ^ ((row >> 1) & 7).
   const int dr = lane >> 3, dpc = lane & 7;
-  const uint32_t xoff_even = (uint32_t)(dr * K * 2 + ((dpc ^ (dr >> 1)) << 4));
-  const uint32_t xoff_odd = (uint32_t)(dr * K * 2 + ((dpc ^ ((dr >> 1) | 4)) << 4));
-  auto dma_x = [&](int kb, int stage) {
+  const uint32_t xg = (uint32_t)((64 * wave + dr) * K * 2 + dpc * 16);
+  const uint32_t xl_even = (uint32_t)((64 * wave + dr) * 128 + ((dpc ^ (dr >> 1)) << 4));
+  const uint32_t xl_odd = (uint32_t)((64 * wave + dr) * 128 + ((dpc ^ ((dr >> 1) | 4)) << 4));
+  auto load_x = [&](int kb, u32x4(&xr)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row0 = 64 * wave + 8 * j;
-      buf_load16_to_lds(rx, xring[stage] + row0 * 128,
-                        ((j & 1) ? xoff_odd : xoff_even) + (uint32_t)(row0 * K * 2 + kb * 128));
-    }
+    for (int j = 0; j < 8; ++j) xr[j] = buf_load16(rx, xg + (uint32_t)(8 * j * K * 2 + kb * 128));
+  };
+  auto store_x = [&](int stage, const u32x4(&xr)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4*>(xring[stage] + ((j & 1) ? xl_odd : xl_even) + 8 * j * 128) = xr[j];
   };
   auto load_w = [&](int kb, u32x4(&c)[2], uint32_t(&q)[2], float(&sv)[2]) {
 #pragma unroll
@@ -111,9 +115,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
     }
   };
-  // Codebook lookups for 8 codes: the byte offset of each code's table entry
-  // is a byte of (x << 2) or (x >> 2).
-  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  // Codebook lookups for 8 codes: the byte address of each code's table
+  // entry is a byte of (x << 2) or (x >> 2).
+  const unsigned char* lutb = smem;
   auto lut8 = [&](uint32_t x, float(&f)[8]) {
     const uint32_t y4 = (x << 2) & 0x3C3C3C3Cu, z4 = (x >> 2) & 0x3C3C3C3Cu;
 #pragma unroll
@@ -149,14 +153,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   float fp[2][8];               // codebook values of a chunk awaiting scale + pack
   float scp[2];                 // the scales of the chunk pending in fp
   bf16x8 xa[8], xb[8];          // X operands, alternating substeps
+  u32x4 xr[8];                  // X tile rows in flight from memory to LDS
 
-  // Prologue: X(0..2) into the ring, W(0) decoded, codes(1) in flight.
-  dma_x(0, 0);
-  dma_x(nk > 1 ? 1 : 0, 1);
-  dma_x(nk > 2 ? 2 : 0, 2);
+  // Prologue: X(0), X(1) in the ring, X(2) in registers, W(0) decoded,
+  // codes(1) in flight.
   load_w(0, cA, qA, sA);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // lut and X(0..2) visible to every wave
+  load_x(0, xr);
+  store_x(0, xr);
+  load_x(nk > 1 ? 1 : 0, xr);
+  store_x(1, xr);
+  load_x(nk > 2 ? 2 : 0, xr);
+  __syncthreads();  // lut and X(0..1) visible to every wave
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const float sc = dq_scale(qA[g], sA[g]);
@@ -192,16 +199,45 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     }                                                                                   \
     __builtin_amdgcn_sched_barrier(0);                                                  \
   }
+  // Substep 3 also writes X(kb+2) from registers to its stage and reloads the
+  // registers with X(kb+3); the writes and loads are spread over the MFMAs.
+#define QLORA_FWD_SUBSTEP3(XCUR, XNXT, NXTSTAGE, WSTAGE, KN3, CA, PACK)                   \
+  {                                                                                     \
+    store_x(WSTAGE, xr);                                                                \
+    load_x(KN3, xr);                                                                    \
+    read_x(NXTSTAGE, 0, XNXT);                                                          \
+    PACK;                                                                               \
+    lut8(CA[0][3], fp[0]);                                                              \
+    lut8(CA[1][3], fp[1]);                                                              \
+    _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
+      acc[0][mi] = mfma32(wc[0][3], XCUR[mi], acc[0][mi]);                              \
+      acc[1][mi] = mfma32(wc[1][3], XCUR[mi], acc[1][mi]);                              \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
+    }                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  }
 
-  // One pipelined step on ring stage ST (the next step's stage is ST1).  CA..
+  // One pipelined step on ring stage ST (the next two steps' stages are ST1,
+  // ST2).  CA..
   // name the register set holding the codes of step kb+1 (decoded now), CB..
   // the set that receives the codes of step kb+2.  The loop is unrolled by
   // six so code sets (period 2) and stages (period 3) are compile-time
   // constants: no register copies (a copy would wait for the load just
   // issued) and statically distinct LDS objects.
-#define QLORA_FWD_STEP(KB, ST, ST1, CA, QA, SA, CB, QB, SB)                                            \
+#define QLORA_FWD_STEP(KB, ST, ST1, ST2, CA, QA, SA, CB, QB, SB)                                       \
   {                                                                                                    \
-    const int st = (ST), st1 = (ST1);                                                                  \
+    const int st = (ST), st1 = (ST1), st2 = (ST2);                                                     \
     const int kn2 = (KB) + 2 < nk ? (KB) + 2 : nk - 1; /* past the end: redundant, in bounds */        \
     const int kn3 = (KB) + 3 < nk ? (KB) + 3 : nk - 1;                                                 \
     load_w(kn2, CB, QB, SB);                                                                           \
@@ -211,14 +247,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
                       { wc[0][3] = pack8(fp[0], scp[0]); wc[1][3] = pack8(fp[1], scp[1]); })            \
     QLORA_FWD_SUBSTEP(1, xb, xa, st, 2, CA, { wn[0][0] = pack8(fp[0], sc0); wn[1][0] = pack8(fp[1], sc1); }) \
     QLORA_FWD_SUBSTEP(2, xa, xb, st, 3, CA, { wn[0][1] = pack8(fp[0], sc0); wn[1][1] = pack8(fp[1], sc1); }) \
-    /* X(kb+1) must be in LDS: of this wave's loads only the 8 X loads of   */                         \
-    /* step kb+2 and the 6 code loads of step kb+2 may still be in flight.  */                         \
-    /* After the barrier every wave is done with stage st, which the loads  */                         \
-    /* of X(kb+3) overwrite.                                                  */                       \
-    asm volatile("s_waitcnt vmcnt(14)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
-    dma_x(kn3, st);                                                                                    \
-    QLORA_FWD_SUBSTEP(3, xb, xa, st1, 0, CA,                                                           \
-                      { wn[0][2] = pack8(fp[0], sc0); wn[1][2] = pack8(fp[1], sc1); })                  \
+    /* Every wave wrote its rows of X(kb+1) one step ago; after the barrier  */                       \
+    /* they are visible, and every wave is done with stage st2 (last read  */                         \
+    /* in step kb-1), which receives X(kb+2).                                */                       \
+    lds_barrier();                                                                                     \
+    QLORA_FWD_SUBSTEP3(xb, xa, st1, st2, kn3, CA,                                                      \
+                       { wn[0][2] = pack8(fp[0], sc0); wn[1][2] = pack8(fp[1], sc1); })                 \
     scp[0] = sc0;                                                                                      \
     scp[1] = sc1;                                                                                      \
     _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                                    \
@@ -226,18 +260,28 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     }                                                                                                  \
   }
 
-  for (int kb = 0; kb < nk; kb += 6) {
-    QLORA_FWD_STEP(kb, 0, 1, cA, qA, sA, cB, qB, sB)
-    if (kb + 1 < nk) QLORA_FWD_STEP(kb + 1, 1, 2, cB, qB, sB, cA, qA, sA)
-    if (kb + 2 < nk) QLORA_FWD_STEP(kb + 2, 2, 0, cA, qA, sA, cB, qB, sB)
-    if (kb + 3 < nk) QLORA_FWD_STEP(kb + 3, 0, 1, cB, qB, sB, cA, qA, sA)
-    if (kb + 4 < nk) QLORA_FWD_STEP(kb + 4, 1, 2, cA, qA, sA, cB, qB, sB)
-    if (kb + 5 < nk) QLORA_FWD_STEP(kb + 5, 2, 0, cB, qB, sB, cA, qA, sA)
+  // Whole groups of six steps loop; the remainder runs once after the loop,
+  // so the loop back-edge is reached from one path only and the wait counts
+  // at its top stay exact.
+  int kb = 0;
+  for (; kb + 6 <= nk; kb += 6) {
+    QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
+    QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
+    QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
+    QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
+    QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
+    QLORA_FWD_STEP(kb + 5, 2, 0, 1, cB, qB, sB, cA, qA, sA)
+  }
+  if (kb < nk) {
+    QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
+    if (kb + 1 < nk) QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
+    if (kb + 2 < nk) QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
+    if (kb + 3 < nk) QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
+    if (kb + 4 < nk) QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
   }
 #undef QLORA_FWD_STEP
 #undef QLORA_FWD_SUBSTEP
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load into LDS may outlive the kernel
-  __syncthreads();
+#undef QLORA_FWD_SUBSTEP3
 
   // LoRA up-projection as one extra K-step of width r: A = B^T (rows n),
   // B operand = s * XA (columns m) as a bf16 hi + lo pair, so the fp32 XA

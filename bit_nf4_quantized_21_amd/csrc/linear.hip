@@ -6,7 +6,8 @@
 //   2. T <= 16: dequant-GEMV;  T > 16: dequant-GEMM; both add s XA B in
 //      their epilogue.
 // Backward (G = dY B^T; dX = dY W' + s G A^T; dA = s X^T G; dB = s XA^T dY):
-//   1. rowdot dY B^T -> G (fp32, workspace)
+//   1. rowdot dY B^T -> G (fp32, workspace) and the transposed bf16 hi / lo
+//      planes of G and of XA that feed the two tokdots
 //   2. tokdot dY^T XA -> dB
 //   3. dequant-GEMM dX with the s G A^T term in its epilogue
 //   4. tokdot X^T G -> dA
@@ -25,44 +26,66 @@ constexpr int64_t kGemvMaxT = 16;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Chunk length along the contraction of a rowdot (X A or dY B^T): enough
-// chunks to give ~256 workgroups, each at least 64 long.
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+int64_t rpad(int32_t r) { return round_up(r, 64); }
+
+// Chunk of the contraction of a rowdot (X A or dY B^T): about 256
+// workgroups of 64 rows each, chunks a multiple of 128 long.
 int64_t row_chunk(int64_t T, int64_t L) {
   const int64_t tiles = cdiv(T, 64);
-  const int64_t target = cdiv(256, tiles);
-  int64_t lc = cdiv(cdiv(L, target), 64) * 64;
-  return lc < 64 ? 64 : lc;
+  int64_t nc = cdiv(256, tiles);
+  const int64_t maxc = cdiv(L, 128);
+  if (nc > maxc) nc = maxc;
+  if (nc < 1) nc = 1;
+  return round_up(cdiv(L, nc), 128);
 }
 
-// Token chunk of a tokdot (X^T G or dY^T XA): ~256 workgroups, >= 32 tokens.
+// Token chunk of a tokdot (X^T G or dY^T XA): about 256 workgroups of 64
+// columns each, chunks a multiple of 128 tokens.
 int64_t tok_chunk(int64_t T, int64_t C) {
   const int64_t tiles = cdiv(C, 64);
-  const int64_t target = cdiv(256, tiles);
-  int64_t tc = cdiv(cdiv(T, target), 32) * 32;
-  return tc < 32 ? 32 : tc;
+  int64_t nc = cdiv(256, tiles);
+  const int64_t maxc = cdiv(T, 128);
+  if (nc > maxc) nc = maxc;
+  if (nc < 1) nc = 1;
+  return round_up(cdiv(T, nc), 128);
+}
+
+// Backward workspace regions, each 256-byte aligned.
+struct BwdLayout {
+  size_t pg, g, planes, ptok, total;
+};
+BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
+  BwdLayout l{};
+  const int64_t RP = rpad(r), TP = round_up(T, 64);
+  l.pg = align256((size_t)cdiv(N, row_chunk(T, N)) * T * RP * sizeof(float));
+  l.g = align256((size_t)T * r * sizeof(float));
+  l.planes = align256((size_t)RP * TP * sizeof(uint16_t));
+  const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * RP * N * sizeof(float);
+  const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * RP * K * sizeof(float);
+  l.ptok = align256(pdb > pda ? pdb : pda);
+  l.total = l.pg + l.g + 4 * l.planes + l.ptok;
+  return l;
 }
 }  // namespace
 
 size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t /*N*/, int32_t r) {
   if (T <= 0) return 0;
-  const int64_t lc = row_chunk(T, K);
-  return align256((size_t)cdiv(K, lc) * T * r * sizeof(float));
+  return align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
 }
 
 size_t bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
   if (T <= 0) return 0;
-  const size_t pg = align256((size_t)cdiv(N, row_chunk(T, N)) * T * r * sizeof(float));
-  const size_t g = align256((size_t)T * r * sizeof(float));
-  const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * N * r * sizeof(float);
-  const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * K * r * sizeof(float);
-  return pg + g + align256(pdb > pda ? pdb : pda);
+  return bwd_layout(T, K, N, r).total;
 }
 
 hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint16_t* X, uint16_t* Y, float* XA,
                              void* ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   float* P = reinterpret_cast<float*>(ws);
-  hipError_t e = launch_rowdot(X, a.A, /*v_kmajor=*/true, P, XA, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
+  RowdotOut o{};
+  o.f32 = XA;
+  hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
   if (e != hipSuccess) return e;
   FwdGemmParams p{};
   p.X = X;
@@ -87,17 +110,30 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
     if (e != hipSuccess) return e;
     return launch_zero_u16(dB, (int64_t)a.r * a.N, s);
   }
+  const BwdLayout l = bwd_layout(a.T, a.K, a.N, a.r);
   char* w = reinterpret_cast<char*>(ws);
-  const int64_t lcg = row_chunk(a.T, a.N);
   float* Pg = reinterpret_cast<float*>(w);
-  w += align256((size_t)cdiv(a.N, lcg) * a.T * a.r * sizeof(float));
-  float* G = reinterpret_cast<float*>(w);
-  w += align256((size_t)a.T * a.r * sizeof(float));
-  float* Ptok = reinterpret_cast<float*>(w);
+  float* G = reinterpret_cast<float*>(w + l.pg);
+  uint16_t* Gth = reinterpret_cast<uint16_t*>(w + l.pg + l.g);
+  uint16_t* Gtl = reinterpret_cast<uint16_t*>(w + l.pg + l.g + l.planes);
+  uint16_t* XAth = reinterpret_cast<uint16_t*>(w + l.pg + l.g + 2 * l.planes);
+  uint16_t* XAtl = reinterpret_cast<uint16_t*>(w + l.pg + l.g + 3 * l.planes);
+  float* Ptok = reinterpret_cast<float*>(w + l.pg + l.g + 4 * l.planes);
+  const int64_t TP = round_up(a.T, 64);
 
-  hipError_t e = launch_rowdot(dY, a.B, /*v_kmajor=*/false, Pg, G, a.T, a.N, a.r, lcg, s);
+  // G = dY B^T (fp32 for the dX epilogue, transposed hi / lo planes for dA),
+  // plus the transposed hi / lo planes of XA for dB.
+  RowdotOut o{};
+  o.f32 = G;
+  o.t_hi = Gth;
+  o.t_lo = Gtl;
+  o.TP = TP;
+  o.side = XA;
+  o.side_hi = XAth;
+  o.side_lo = XAtl;
+  hipError_t e = launch_rowdot(dY, a.B, /*v_lr=*/false, Pg, o, a.T, a.N, a.r, row_chunk(a.T, a.N), s);
   if (e != hipSuccess) return e;
-  e = launch_tokdot(dY, XA, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*transpose=*/true, s);
+  e = launch_tokdot(dY, XAth, XAtl, TP, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*m_major=*/false, s);
   if (e != hipSuccess) return e;
   DxGemmParams p{};
   p.dY = dY;
@@ -114,7 +150,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   p.s = a.s;
   e = launch_gemm_dx(p, cb, s);
   if (e != hipSuccess) return e;
-  return launch_tokdot(X, G, Ptok, dA, a.T, a.K, a.r, tok_chunk(a.T, a.K), a.s, /*transpose=*/false, s);
+  return launch_tokdot(X, Gth, Gtl, TP, Ptok, dA, a.T, a.K, a.r, tok_chunk(a.T, a.K), a.s, /*m_major=*/true, s);
 }
 
 }  // namespace qlora

@@ -1,165 +1,395 @@
-// Skinny rank-r GEMMs of the LoRA adapter for gfx950 (LoRA tutorial,
-// weight-update section: dW = W_A W_B; QLoRA abstract: gradients flow into
-// the adapters only).
+// Skinny rank-r products of the LoRA adapter for gfx950 (LoRA tutorial,
+// weight-update section: dW = W_A W_B with the alpha/r scale; QLoRA abstract:
+// the frozen 4-bit base passes gradients into the adapters only).
 //
-//   rowdot:  P[c][t][j] = sum_{l in chunk c} M[t][l] V(j,l)      (XA = X A,  G = dY B^T)
-//   tokdot:  P[c][m][j] = sum_{t in chunk c} M[t][m] S[t][j]      (dA ~ X^T G, dB^T ~ dY^T XA)
-// followed by fixed-order reductions of the chunk partials (deterministic,
-// no float atomics).  All are HBM-bound streams over X or dY; the products
-// run on bf16 MFMA 16x16x32 with fp32 accumulation.  The fp32 factors S (XA
-// and G) enter the MFMA as a bf16 hi + lo pair, which keeps the adapter
-// gradients at ~16-bit operand precision.
+//   rowdot:  out[t][j] = sum_l M[t][l] V(l, j)     XA = X A,   G = dY B^T
+//   tokdot:  out[m][j] = s sum_t M[t][m] S[t][j]   dA = s X^T G,  dB^T = s dY^T XA
+//
+// Both stream a tall bf16 matrix M (X or dY) once from HBM; the rank-r
+// factor is small and stays in L2.  Each is split into chunks of the
+// contraction whose fp32 partials are summed in a fixed order by a second
+// kernel, so results are bitwise reproducible (no float atomics).
+//
+// Products run on bf16 MFMA 16x16x32 with fp32 accumulation.  The MFMA wants
+// 8 consecutive contraction indices per lane; where the contraction runs
+// across rows of a row-major operand (A's rows in X A, the token rows of M in
+// tokdot) each lane loads an 8 x 4 block and transposes it in registers with
+// byte permutes, so lane p of an MFMA serves column 4p + c for c = 0..3 and
+// the four MFMAs c together cover 64 columns.  The fp32 factors of tokdot
+// (G, XA) enter as bf16 hi + lo planes written by the rowdot reduction.
 #include "common.hpp"
-#include "timing.hpp"
 #include "lora.hpp"
+#include "timing.hpp"
 
 namespace qlora {
 
+namespace {
+
+// Operand c (c = 0..3) of a lane's 8 x 4 bf16 block: rows i = 0..7 hold
+// columns 4p .. 4p+3 as two dwords (cols 0,1 | cols 2,3); the operand packs
+// column c of the 8 rows, row 2q in the low half of dword q.
+__device__ __forceinline__ bf16x8 column_of(const uint2 (&rows)[8], int c) {
+  const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+  uint32_t d[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = (c & 2) ? rows[2 * q].y : rows[2 * q].x;
+    const uint32_t hi = (c & 2) ? rows[2 * q + 1].y : rows[2 * q + 1].x;
+    d[q] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+  return as_bf16x8(d[0], d[1], d[2], d[3]);
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
-// rowdot.  One workgroup = 4 waves = 64 rows t of M; wave w owns rows
-// [t0+16w, t0+16w+16) and every j.  MFMA orientation: D[j][t] (A = V^T, B = M).
-// Lane (l16, g): A-operand row j = 16*jt + l16, B-operand column t = l16;
-// both hold the 8 consecutive l = ks + 8g .. ks + 8g + 7.
+// rowdot partials.  Workgroup = 4 waves = 64 rows t of M x one chunk of l;
+// wave w takes the w-th quarter of the chunk, 32 l per step.  MFMA
+// orientation D[t][j]: A operand = M (row t = t0 + 16 tt + p, 8 consecutive
+// l), B operand = V (8 consecutive l of column j = 64 jb + 4p + c).
+// V_LR: V is stored [L][r] (the LoRA A); else [r][L] (the LoRA B).
+// P[c][t][j] has row stride RP = 64 * JB.
 // ---------------------------------------------------------------------------
-template <bool VKMAJOR>
+template <bool V_LR, int JB>
 __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __restrict__ M,
                                                              const uint16_t* __restrict__ V, float* __restrict__ P,
                                                              int64_t T, int64_t L, int r, int64_t LC) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int64_t t = (int64_t)blockIdx.x * 64 + 16 * wave + l16;
-  const int64_t c = blockIdx.y;
-  const int64_t lbeg = c * LC;
-  const int64_t lend = (lbeg + LC < L) ? lbeg + LC : L;
-  const int njt = (r + 15) / 16;  // <= 8
-  f32x4 acc[8];
+  __shared__ __align__(16) float red[4][64 * 64];
+  constexpr int RP = 64 * JB;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane & 15, g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int64_t ch = blockIdx.y;
+  const int64_t lbeg = ch * LC;
+  const int64_t lend = lbeg + LC < L ? lbeg + LC : L;
+  const int64_t LW = LC / 4;
+  const int64_t wl0 = lbeg + wave * LW;
+  const int64_t wl1 = wl0 + LW < lend ? wl0 + LW : lend;
+  const int nsteps = wl1 > wl0 ? (int)((wl1 - wl0 + 31) / 32) : 0;
+
+  f32x4 acc[JB][4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool tvalid = t < T;
-  for (int64_t ks = lbeg; ks < lend; ks += 32) {
-    const int64_t l0 = ks + 8 * g;
-    const bool lvalid = l0 < lend;  // L % 8 == 0: an 8-group is whole or absent
-    u32x4 mv = {0u, 0u, 0u, 0u};
-    if (tvalid && lvalid) mv = *reinterpret_cast<const u32x4*>(M + t * L + l0);
-    const bf16x8 bop = as_bf16x8(mv);
+  for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt < njt) {
-        const int j = 16 * jt + l16;
-        u32x4 vv = {0u, 0u, 0u, 0u};
-        if (j < r && lvalid) {
-          if (VKMAJOR) {
-            uint32_t e[8];
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = V[(l0 + i) * r + j];
-            vv = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-          } else {
-            vv = *reinterpret_cast<const u32x4*>(V + (int64_t)j * L + l0);
-          }
+      for (int c = 0; c < 4; ++c) acc[jb][tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Regs {
+    u32x4 m[4];
+    u32x4 v[JB][4];   // V_LR == false: the operands themselves
+    uint2 a[JB][8];   // V_LR: 8 rows x 4 columns per j-block, transposed at use
+  };
+  auto load = [&](int s, Regs& R) {
+    const int64_t l = wl0 + 32 * s + 8 * g;
+    const bool lv = l < wl1;  // L % 8 == 0: an 8-group is whole or absent
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int64_t t = t0 + 16 * tt + p;
+      R.m[tt] = (lv && t < T) ? *reinterpret_cast<const u32x4*>(M + t * L + l) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      if constexpr (V_LR) {
+        const int j = 64 * jb + 4 * p;
+        const bool ok = lv && j < r;  // r % 8 == 0: a 4-group is whole or absent
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          R.a[jb][i] = ok ? *reinterpret_cast<const uint2*>(V + (l + i) * r + j) : make_uint2(0u, 0u);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 64 * jb + 4 * p + c;
+          R.v[jb][c] = (lv && j < r) ? *reinterpret_cast<const u32x4*>(V + (int64_t)j * L + l)
+                                     : u32x4{0u, 0u, 0u, 0u};
         }
-        acc[jt] = mfma16(as_bf16x8(vv), bop, acc[jt]);
+      }
+    }
+  };
+  auto compute = [&](const Regs& R) {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 vop = V_LR ? column_of(R.a[jb], c) : as_bf16x8(R.v[jb][c]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[jb][tt][c] = mfma16(as_bf16x8(R.m[tt]), vop, acc[jb][tt][c]);
+      }
+    }
+  };
+
+  // Two register sets: the loads of step s+1 are in flight while step s runs.
+  Regs RA, RB;
+  load(0, RA);
+  for (int s = 0; s < nsteps; s += 2) {
+    load(s + 1, RB);
+    compute(RA);
+    load(s + 2, RA);
+    compute(RB);
+  }
+
+  // Sum the four waves' partials in wave order and store this chunk's tile.
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) {
+    if (jb) __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tt + 4 * g + i;
+        *reinterpret_cast<float4*>(&red[wave][t * 64 + 4 * p]) =
+            make_float4(acc[jb][tt][0][i], acc[jb][tt][1][i], acc[jb][tt][2][i], acc[jb][tt][3][i]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = threadIdx.x + 256 * k;
+      const int t = q >> 4, j4 = q & 15;
+      if (t0 + t >= T) continue;
+      float4 sum = *reinterpret_cast<const float4*>(&red[0][t * 64 + 4 * j4]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum = add4(sum, *reinterpret_cast<const float4*>(&red[w][t * 64 + 4 * j4]));
+      *reinterpret_cast<float4*>(P + (ch * T + t0 + t) * RP + 64 * jb + 4 * j4) = sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rowdot reduction: v[t][j] = sum over chunks (in chunk order), then any of
+//   f32      [T][r]  fp32 result
+//   row_hi/lo[T][RP] bf16 split of scale_row * v (zero for j >= r)
+//   t_hi/lo  [RP][TP] bf16 split of v, transposed (zero outside T x r)
+//   side -> side_hi/lo: the same transposed split of an extra fp32 [T][r]
+//   matrix (XA in the backward pass), since it covers the same tile.
+// Workgroup = a 64 t x 64 j tile; thread q handles 4 consecutive j of one t.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const float* __restrict__ P, int64_t T,
+                                                            int r, int RP, int nc) {
+  __shared__ __align__(16) uint16_t tr[4][64 * 72];  // [plane][j][t], t padded to 72
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int jb = blockIdx.y;
+  const bool want_t = o.t_hi != nullptr, want_side = o.side != nullptr;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int t = q >> 4, j = 64 * jb + 4 * (q & 15);
+    const int64_t tg = t0 + t;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tg < T) {
+      float4 part[8];
+      for (int c0 = 0; c0 < nc; c0 += 8) {
+        const int n = nc - c0 < 8 ? nc - c0 : 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * T + tg) * RP + j);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
+      }
+      if (o.f32 && j < r) *reinterpret_cast<float4*>(o.f32 + tg * r + j) = v;
+      if (o.row_hi) {
+        const float sv[4] = {v.x * o.scale_row, v.y * o.scale_row, v.z * o.scale_row, v.w * o.scale_row};
+        const uint32_t h0 = pack_bf16x2(sv[0], sv[1]), h1 = pack_bf16x2(sv[2], sv[3]);
+        const uint32_t l0 = pack_bf16x2(sv[0] - bf16_lo(h0), sv[1] - bf16_hi(h0));
+        const uint32_t l1 = pack_bf16x2(sv[2] - bf16_lo(h1), sv[3] - bf16_hi(h1));
+        *reinterpret_cast<uint2*>(o.row_hi + tg * RP + j) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(o.row_lo + tg * RP + j) = make_uint2(l0, l1);
+      }
+    }
+    if (want_t) {
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h = pack_bf16x2(vv[e], 0.f) & 0xFFFFu;
+        const uint32_t l = pack_bf16x2(vv[e] - __uint_as_float(h << 16), 0.f) & 0xFFFFu;
+        tr[0][(j - 64 * jb + e) * 72 + t] = (uint16_t)h;
+        tr[1][(j - 64 * jb + e) * 72 + t] = (uint16_t)l;
+      }
+    }
+    if (want_side) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tg < T && j < r) x = *reinterpret_cast<const float4*>(o.side + tg * r + j);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h = pack_bf16x2(xv[e], 0.f) & 0xFFFFu;
+        const uint32_t l = pack_bf16x2(xv[e] - __uint_as_float(h << 16), 0.f) & 0xFFFFu;
+        tr[2][(j - 64 * jb + e) * 72 + t] = (uint16_t)h;
+        tr[3][(j - 64 * jb + e) * 72 + t] = (uint16_t)l;
       }
     }
   }
-  if (!tvalid) return;
-  // D[j][t]: this lane holds column t and rows j = 16*jt + 4g + i.
+  if (!want_t && !want_side) return;  // uniform per workgroup
+  __syncthreads();
+  // Transposed planes: thread q writes 8 consecutive t of row j.
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
-    const int j = 16 * jt + 4 * g;
-    if (jt < njt && j < r) {
-      float4 o = make_float4(acc[jt][0], acc[jt][1], acc[jt][2], acc[jt][3]);
-      *reinterpret_cast<float4*>(P + (c * T + t) * r + j) = o;
+  for (int k = 0; k < 2; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int j = q >> 3, t8 = 8 * (q & 7);
+    const int64_t off = (int64_t)(64 * jb + j) * o.TP + t0 + t8;
+    if (want_t) {
+      *reinterpret_cast<u32x4*>(o.t_hi + off) = *reinterpret_cast<const u32x4*>(&tr[0][j * 72 + t8]);
+      *reinterpret_cast<u32x4*>(o.t_lo + off) = *reinterpret_cast<const u32x4*>(&tr[1][j * 72 + t8]);
+    }
+    if (want_side) {
+      *reinterpret_cast<u32x4*>(o.side_hi + off) = *reinterpret_cast<const u32x4*>(&tr[2][j * 72 + t8]);
+      *reinterpret_cast<u32x4*>(o.side_lo + off) = *reinterpret_cast<const u32x4*>(&tr[3][j * 72 + t8]);
     }
   }
 }
 
-// out[t][j] = sum_c P[c][t][j], fixed order.  One thread per 4 outputs.
-__global__ __launch_bounds__(256) void rowdot_reduce_kernel(const float* __restrict__ P, float* __restrict__ out,
-                                                            int64_t T, int r, int nc) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total4 = T * r / 4;
-  if (q >= total4) return;
-  float4 s = *reinterpret_cast<const float4*>(P + 4 * q);
-  for (int c = 1; c < nc; ++c) {
-    const float4 v = *reinterpret_cast<const float4*>(P + (int64_t)c * T * r + 4 * q);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
-  *reinterpret_cast<float4*>(out + 4 * q) = s;
-}
-
 // ---------------------------------------------------------------------------
-// tokdot.  One workgroup = 4 waves = 64 columns m of M; wave w owns columns
-// [m0+16w, m0+16w+16).  MFMA orientation: D[j][m] (A = S^T as hi+lo, B = M).
-// Lane (l16, g) holds tokens t = ts + 8g .. ts + 8g + 7 of its row / column.
+// tokdot partials.  Workgroup = 4 waves = 64 columns m x one chunk of t;
+// wave w takes the w-th quarter of the chunk, 32 t per step.  MFMA
+// orientation D[j][m]: A operand = S^T from the transposed hi / lo planes
+// (row j = 16 jt + p, 8 consecutive t), B operand = M transposed in
+// registers (8 consecutive t of column m = m0 + 4p + c).
+// P[c][j][m] has RP rows per chunk.
 // ---------------------------------------------------------------------------
+template <int JT>
 __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __restrict__ M,
-                                                             const float* __restrict__ S, float* __restrict__ P,
-                                                             int64_t T, int64_t C, int r, int64_t TC) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int64_t m = (int64_t)blockIdx.x * 64 + 16 * wave + l16;
-  const int64_t c = blockIdx.y;
-  const int64_t tbeg = c * TC;
-  const int64_t tend = (tbeg + TC < T) ? tbeg + TC : T;
-  const int njt = (r + 15) / 16;
-  const bool mvalid = m < C;
-  f32x4 acc[8];
+                                                             const uint16_t* __restrict__ Sh,
+                                                             const uint16_t* __restrict__ Sl, int64_t TP,
+                                                             float* __restrict__ P, int64_t T, int64_t C,
+                                                             int64_t TC) {
+  __shared__ __align__(16) float red[4][64 * 64];
+  constexpr int RP = 16 * JT;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int64_t ch = blockIdx.y;
+  const int64_t tbeg = ch * TC;
+  const int64_t tend = tbeg + TC < T ? tbeg + TC : T;
+  const int64_t TW = TC / 4;
+  const int64_t wt0 = tbeg + wave * TW;
+  const int64_t wt1 = wt0 + TW < tend ? wt0 + TW : tend;
+  const int nsteps = wt1 > wt0 ? (int)((wt1 - wt0 + 31) / 32) : 0;
+  const int64_t m = m0 + 4 * p;
+  const bool mv = m < C;  // C % 8 == 0: a 4-group is whole or absent
+
+  f32x4 acc[JT][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t ts = tbeg; ts < tend; ts += 32) {
-    const int64_t t0 = ts + 8 * g;
-    uint32_t e[8];
+  for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = (mvalid && t0 + i < tend) ? M[(t0 + i) * C + m] : 0u;
-    const bf16x8 bop =
-        as_bf16x8(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+    for (int c = 0; c < 4; ++c) acc[jt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Regs {
+    uint2 a[8];
+    u32x4 h[JT], l[JT];
+  };
+  auto load = [&](int s, Regs& R) {
+    const int64_t t = wt0 + 32 * s + 8 * g;
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt < njt) {
-        const int j = 16 * jt + l16;
-        float v[8];
+    for (int i = 0; i < 8; ++i)
+      R.a[i] = (mv && t + i < wt1) ? *reinterpret_cast<const uint2*>(M + (t + i) * C + m) : make_uint2(0u, 0u);
+    // The planes are zero for t >= T and hold TP >= T columns, so the loads
+    // need no token mask; steps past this wave's range are masked via M.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (j < r && t0 + i < tend) ? S[(t0 + i) * r + j] : 0.0f;
-        bf16x8 hi, lo;
-        split_bf16x8(v, hi, lo);
-        acc[jt] = mfma16(hi, bop, acc[jt]);
-        acc[jt] = mfma16(lo, bop, acc[jt]);
+    for (int jt = 0; jt < JT; ++jt) {
+      const int64_t off = (int64_t)(16 * jt + p) * TP + (t < tend ? t : tbeg);
+      R.h[jt] = *reinterpret_cast<const u32x4*>(Sh + off);
+      R.l[jt] = *reinterpret_cast<const u32x4*>(Sl + off);
+    }
+  };
+  auto compute = [&](const Regs& R) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 mop = column_of(R.a, c);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        acc[jt][c] = mfma16(as_bf16x8(R.h[jt]), mop, acc[jt][c]);
+        acc[jt][c] = mfma16(as_bf16x8(R.l[jt]), mop, acc[jt][c]);
       }
     }
+  };
+
+  Regs RA, RB;
+  load(0, RA);
+  for (int s = 0; s < nsteps; s += 2) {
+    load(s + 1, RB);
+    compute(RA);
+    load(s + 2, RA);
+    compute(RB);
   }
-  if (!mvalid) return;
+
+  // D[j][m]: lane holds rows j = 16 jt + 4g + i, column m = m0 + 4p + c.
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
-    const int j = 16 * jt + 4 * g;
-    if (jt < njt && j < r) {
-      float4 o = make_float4(acc[jt][0], acc[jt][1], acc[jt][2], acc[jt][3]);
-      *reinterpret_cast<float4*>(P + (c * C + m) * r + j) = o;
+  for (int jb = 0; jb < RP / 64 + (RP % 64 ? 1 : 0); ++jb) {
+    if (jb) __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      if (4 * jb + jt >= JT) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * jt + 4 * g + i;
+        const f32x4* a = acc[4 * jb + jt];
+        *reinterpret_cast<float4*>(&red[wave][j * 64 + 4 * p]) = make_float4(a[0][i], a[1][i], a[2][i], a[3][i]);
+      }
+    }
+    __syncthreads();
+    const int rows = RP - 64 * jb < 64 ? RP - 64 * jb : 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = threadIdx.x + 256 * k;
+      const int j = q >> 4, m4 = q & 15;
+      if (j >= rows || m0 + 4 * m4 >= C) continue;
+      float4 sum = *reinterpret_cast<const float4*>(&red[0][j * 64 + 4 * m4]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum = add4(sum, *reinterpret_cast<const float4*>(&red[w][j * 64 + 4 * m4]));
+      *reinterpret_cast<float4*>(P + (ch * RP + 64 * jb + j) * C + m0 + 4 * m4) = sum;
     }
   }
 }
 
-// out = bf16(s * sum_c P[c][m][j]); layout [m][j] (dA: [K,r]) or [j][m]
-// (dB: [r,N]).  One thread per 4 consecutive j.
+// out = bf16(s * sum over chunks of P[c][j][m]), stored [j][m] (dB: [r,N]) or
+// [m][j] (dA: [K,r]).  Workgroup = a 64 j x 64 m tile.
 __global__ __launch_bounds__(256) void tokdot_reduce_kernel(const float* __restrict__ P, uint16_t* __restrict__ out,
-                                                            int64_t C, int r, int nc, float s, int transpose) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total4 = C * r / 4;
-  if (q >= total4) return;
-  float4 a = *reinterpret_cast<const float4*>(P + 4 * q);
-  for (int c = 1; c < nc; ++c) {
-    const float4 v = *reinterpret_cast<const float4*>(P + (int64_t)c * C * r + 4 * q);
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+                                                            int64_t C, int r, int RP, int nc, float s,
+                                                            int m_major) {
+  __shared__ __align__(16) uint16_t tr[64 * 72];  // [m][j], j padded to 72
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int jb = blockIdx.y;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int j = q >> 4, m4 = 4 * (q & 15);
+    const int jg = 64 * jb + j;
+    const int64_t mg = m0 + m4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jg < r && mg < C) {
+      float4 part[8];
+      for (int c0 = 0; c0 < nc; c0 += 8) {
+        const int n = nc - c0 < 8 ? nc - c0 : 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * RP + jg) * C + mg);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
+      }
+    }
+    const uint32_t p0 = pack_bf16x2(v.x * s, v.y * s), p1 = pack_bf16x2(v.z * s, v.w * s);
+    if (!m_major) {
+      if (jg < r && mg < C) *reinterpret_cast<uint2*>(out + (int64_t)jg * C + mg) = make_uint2(p0, p1);
+    } else {
+      tr[(m4 + 0) * 72 + j] = (uint16_t)(p0 & 0xFFFFu);
+      tr[(m4 + 1) * 72 + j] = (uint16_t)(p0 >> 16);
+      tr[(m4 + 2) * 72 + j] = (uint16_t)(p1 & 0xFFFFu);
+      tr[(m4 + 3) * 72 + j] = (uint16_t)(p1 >> 16);
+    }
   }
-  const uint32_t p0 = pack_bf16x2(a.x * s, a.y * s), p1 = pack_bf16x2(a.z * s, a.w * s);
-  const int64_t m = (4 * q) / r;
-  const int j = (int)((4 * q) % r);
-  if (!transpose) {
-    *reinterpret_cast<uint2*>(out + 4 * q) = make_uint2(p0, p1);
-  } else {
-    out[(int64_t)(j + 0) * C + m] = (uint16_t)(p0 & 0xFFFF);
-    out[(int64_t)(j + 1) * C + m] = (uint16_t)(p0 >> 16);
-    out[(int64_t)(j + 2) * C + m] = (uint16_t)(p1 & 0xFFFF);
-    out[(int64_t)(j + 3) * C + m] = (uint16_t)(p1 >> 16);
+  if (!m_major) return;  // uniform per launch
+  __syncthreads();
+  // Thread q writes 4 consecutive j of row m.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int mm = q >> 4, j4 = 4 * (q & 15);
+    const int jg = 64 * jb + j4;
+    if (m0 + mm < C && jg < r)
+      *reinterpret_cast<uint2*>(out + (m0 + mm) * r + jg) = *reinterpret_cast<const uint2*>(&tr[mm * 72 + j4]);
   }
 }
 
@@ -171,44 +401,50 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* __restrict__ p,
 
 // ---------------------------------------------------------------------------
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_kmajor, float* P, float* out, int64_t T,
+hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
                          int64_t L, int r, int64_t LC, hipStream_t s) {
-  const int64_t nc = (L + LC - 1) / LC;
-  dim3 grid((unsigned)((T + 63) / 64), (unsigned)nc);
-  if (v_kmajor)
-    {
-      KernelTimer kt_("rowdot_partial_kernel", s);
-      hipLaunchKernelGGL(rowdot_partial_kernel<true>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+  const int64_t nc = cdiv(L, LC);
+  const int JB = r > 64 ? 2 : 1;
+  dim3 grid((unsigned)cdiv(T, 64), (unsigned)nc);
+  {
+    KernelTimer kt_("rowdot_partial_kernel", s);
+    if (v_lr) {
+      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<true, 1>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+      else hipLaunchKernelGGL((rowdot_partial_kernel<true, 2>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+    } else {
+      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<false, 1>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+      else hipLaunchKernelGGL((rowdot_partial_kernel<false, 2>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
     }
-  else
-    {
-      KernelTimer kt_("rowdot_partial_kernel", s);
-      hipLaunchKernelGGL(rowdot_partial_kernel<false>, grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
-    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("rowdot_reduce_kernel", s);
-    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3(blocks_for(T * r / 4)), dim3(256), 0, s, P, out, T, r, (int)nc);
+    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)cdiv(T, 64), (unsigned)JB), dim3(256), 0, s, o, P, T, r,
+                       64 * JB, (int)nc);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_tokdot(const uint16_t* M, const float* S, float* P, uint16_t* out, int64_t T, int64_t C, int r,
-                         int64_t TC, float scale, bool transpose, hipStream_t s) {
-  const int64_t nc = (T + TC - 1) / TC;
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)nc);
+hipError_t launch_tokdot(const uint16_t* M, const uint16_t* Sh, const uint16_t* Sl, int64_t TP, float* P,
+                         uint16_t* out, int64_t T, int64_t C, int r, int64_t TC, float scale, bool m_major,
+                         hipStream_t s) {
+  const int64_t nc = cdiv(T, TC);
+  const int JT = cdiv(r, 16) <= 4 ? 4 : 8;
+  dim3 grid((unsigned)cdiv(C, 64), (unsigned)nc);
   {
     KernelTimer kt_("tokdot_partial_kernel", s);
-    hipLaunchKernelGGL(tokdot_partial_kernel, grid, dim3(256), 0, s, M, S, P, T, C, r, TC);
+    if (JT == 4) hipLaunchKernelGGL(tokdot_partial_kernel<4>, grid, dim3(256), 0, s, M, Sh, Sl, TP, P, T, C, TC);
+    else hipLaunchKernelGGL(tokdot_partial_kernel<8>, grid, dim3(256), 0, s, M, Sh, Sl, TP, P, T, C, TC);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("tokdot_reduce_kernel", s);
-    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3(blocks_for(C * r / 4)), dim3(256), 0, s, P, out, C, r, (int)nc,
-                     scale, transpose ? 1 : 0);
+    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(r, 64)), dim3(256), 0, s, P,
+                       out, C, r, 16 * JT, (int)nc, scale, m_major ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,220 @@
+"""Workload and summariser for rocprofv3 measurements of the NF4 linear kernels.
+
+`run` launches, on cuda:0, a few steps of the 7B MLP workload (gate/up
+4096->11008, down 11008->4096, 2048 tokens, LoRA r=64, fwd + bwd), a few
+small-token forwards (4096x4096, 4 tokens), and a plain copy of a known number
+of bytes that calibrates the HBM byte counters:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o fetch -- \
+        python bit_nf4_quantized_21_amd/profile_run.py run
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o write -- \
+        python bit_nf4_quantized_21_amd/profile_run.py run
+
+`traffic` turns the two counter CSVs into per-kernel HBM bytes per launch,
+scaled by what the same counters read for the copy, and writes
+profiles/traffic_<kernel>_<workload>.json (with a hash of the kernel sources
+it was measured on) and a readable profiles/traffic_<workload>.md.
+
+`stats` turns a `rocprofv3 --kernel-trace --stats --output-format csv` kernel
+statistics file into a short markdown table.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_nf4_quantized_21_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+COPY_BYTES = 512 << 20
+MLP = (("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008))
+T_MLP, R, ALPHA = 2048, 64, 16.0
+GEMV = (4, 4096, 4096)
+
+# kernel -> (workload tag, sources it is built from)
+KERNEL_SOURCES = {
+    "gemm_fwd_kernel": ("mlp7b", ["gemm_fwd.hip", "gemm.hpp", "common.hpp"]),
+    "gemm_dx_kernel": ("mlp7b", ["gemm_dx.hip", "gemm.hpp", "common.hpp"]),
+    "tokdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
+    "rowdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
+    "gemv_fwd_kernel": ("gemv7b", ["gemv.hip", "gemm.hpp", "common.hpp"]),
+}
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dq_bytes(N, K):
+    nb = N * K // 64
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256)
+
+
+def algorithmic_bytes(kernel, T, N, K, r):
+    """Each operand the kernel must touch, read or written once."""
+    if kernel == "gemm_fwd_kernel":
+        return 2 * T * K + dq_bytes(N, K) + 2 * r * N + 4 * T * r + 2 * T * N
+    if kernel == "gemm_dx_kernel":
+        return 2 * T * N + dq_bytes(N, K) + 2 * K * r + 4 * T * r + 2 * T * K
+    if kernel == "gemv_fwd_kernel":
+        return 2 * T * K + dq_bytes(N, K) + 2 * r * N + 4 * T * r + 2 * T * N
+    return None
+
+
+def run(steps):
+    import torch
+    from bit_nf4_quantized_21_amd import qlora, synth
+    qlora.lib()
+    dev = torch.device("cuda", 0)
+    layers = []
+    for i, (_, N, K) in enumerate(MLP):
+        inp = synth.device_inputs(T_MLP, N, K, R, i, backward=True)
+        codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
+        q8, s2 = qlora.double_quant(absmax)
+        del inp["W"], absmax
+        L = dict(N=N, codes=codes, q8=q8, s2=s2, **inp)
+        L["wsf"] = torch.empty(max(1, qlora.linear_fwd_workspace_bytes(T_MLP, K, N, R)), dtype=torch.uint8, device=dev)
+        L["wsb"] = torch.empty(max(1, qlora.linear_bwd_workspace_bytes(T_MLP, K, N, R)), dtype=torch.uint8, device=dev)
+        layers.append(L)
+    for _ in range(steps):
+        for L in layers:
+            Y, XA = qlora.linear_fwd(L["X"], L["codes"], L["q8"], L["s2"], L["A"], L["B"], ALPHA, L["N"],
+                                     workspace=L["wsf"])
+            qlora.linear_bwd(L["dY"], L["X"], XA, L["codes"], L["q8"], L["s2"], L["A"], L["B"], ALPHA,
+                             workspace=L["wsb"])
+    torch.cuda.synchronize()
+    del layers
+    T, N, K = GEMV
+    inp = synth.device_inputs(T, N, K, R, 0, backward=False)
+    codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
+    q8, s2 = qlora.double_quant(absmax)
+    for _ in range(steps):
+        qlora.linear_fwd(inp["X"], codes, q8, s2, inp["A"], inp["B"], ALPHA, N)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile_run done", flush=True)
+
+
+def short_name(name):
+    n = name.split("(")[0].strip()
+    if n.startswith("void "):
+        n = n[5:]
+    return n.split("<")[0].split("::")[-1]
+
+
+def read_counter(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    rows.append((row["Kernel_Name"], int(row["Grid_Size"]), float(row["Counter_Value"])))
+    return rows
+
+
+def copy_factor(rows):
+    """Counter KiB per true KiB for the copy of COPY_BYTES."""
+    vals = [v for (k, g, v) in rows if "copy" in k.lower() and v > 0.5 * COPY_BYTES / 1024]
+    if not vals:
+        raise SystemExit("copy kernel not found in counters")
+    return (sum(vals) / len(vals)) / (COPY_BYTES / 1024)
+
+
+def traffic(fetch_dir, write_dir, command):
+    fr, wr = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
+    ff, wf = copy_factor(fr), copy_factor(wr)
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (from the repository root):", "", "```", command, "```", "",
+             f"Counter scale from a plain {COPY_BYTES >> 20} MiB device copy: FETCH_SIZE reads "
+             f"{ff:.4f}x, WRITE_SIZE {wf:.4f}x the true bytes; the figures below are divided by these.", "",
+             "| kernel | workload | launches | fetch MB | write MB | total MB/launch | algorithmic MB/launch | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    for kernel, (wl, sources) in KERNEL_SOURCES.items():
+        f = [v for (k, g, v) in fr if short_name(k) == kernel]
+        w = [v for (k, g, v) in wr if short_name(k) == kernel]
+        if not f or not w:
+            continue
+        fb = sum(f) / len(f) * 1024 / ff
+        wb = sum(w) / len(w) * 1024 / wf
+        if wl == "mlp7b":
+            alg = [algorithmic_bytes(kernel, T_MLP, N, K, R) for (_, N, K) in MLP]
+        else:
+            alg = [algorithmic_bytes(kernel, *GEMV, R)]
+        alg_b = None if alg[0] is None else sum(alg) / len(alg)
+        rec = {"kernel": kernel, "workload": wl, "launches": len(f), "fetch_bytes_per_launch": round(fb),
+               "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb),
+               "algorithmic_bytes_per_launch": alg_b, "copy_factor_fetch": round(ff, 5),
+               "copy_factor_write": round(wf, 5), "sources": sources, "source_hash": source_hash(*sources),
+               "command": command}
+        with open(os.path.join(PROFILES, f"traffic_{kernel}_{wl}.json"), "w") as fo:
+            json.dump(rec, fo, indent=1)
+        ratio = "" if alg_b is None else f"{(fb + wb) / alg_b:.2f}"
+        algs = "" if alg_b is None else f"{alg_b / 1e6:.1f}"
+        lines.append(f"| {kernel} | {wl} | {len(f)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | "
+                     f"{algs} | {ratio} |")
+    with open(os.path.join(PROFILES, "traffic_mlp7b_gemv7b.md"), "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats(stats_csv, out_md, command, top=12):
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "", "Command (from the repository root):",
+             "", "```", command, "```", "",
+             "| kernel | calls | total ms | average us | min us | max us | share % |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        lines.append(f"| {short_name(r['Name'])[:60]} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--steps", type=int, default=2)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--command", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("out_md")
+    s.add_argument("--command", required=True)
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run(a.steps)
+    elif a.cmd == "traffic":
+        traffic(a.fetch_dir, a.write_dir, a.command)
+    else:
+        stats(a.stats_csv, a.out_md, a.command)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
