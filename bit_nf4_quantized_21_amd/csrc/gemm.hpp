@@ -28,16 +28,27 @@ struct DxGemmParams {
   const uint8_t* q8;
   const float* s2;
   const uint16_t* A;     // [K,r] bf16
-  const float* G;        // [T,r] fp32
+  const uint16_t* Gh;    // [T,RP] bf16 hi part of s*G (G = dY B^T), zero past r
+  const uint16_t* Gl;    // [T,RP] bf16 lo part
   uint16_t* dX;          // [T,K] bf16
   int64_t T, K, N;
-  int r;
-  float s;
-  int tiles_k, tiles_t, per_xcd;
+  int r, RP;            // RP = r rounded up to 64
+  float* slots;          // split partials: tiles * S * 65536 floats (S > 1)
+  int* counters;         // one per tile, zero on entry, left zero
+  int S;                 // contraction slices per tile
+  int tiles_k, tiles_t, per_xcd, steps_per;
 };
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
 hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
 hipError_t launch_gemm_dx(const DxGemmParams& p, const Codebook& cb, hipStream_t s);
+
+// Tile grid of the dX GEMM: tiles and contraction slices for a T x K x N
+// problem (the workspace of the backward pass is sized from these).
+struct DxGrid {
+  int64_t tiles;
+  int S;
+};
+DxGrid dx_grid(int64_t T, int64_t K, int64_t N);
 
 }  // namespace qlora

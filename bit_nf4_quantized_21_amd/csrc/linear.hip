@@ -6,8 +6,8 @@
 //   2. T <= 16: dequant-GEMV;  T > 16: dequant-GEMM; both add s XA B in
 //      their epilogue.
 // Backward (G = dY B^T; dX = dY W' + s G A^T; dA = s X^T G; dB = s XA^T dY):
-//   1. rowdot dY B^T -> G (fp32, workspace) and the transposed bf16 hi / lo
-//      planes of G and of XA that feed the two tokdots
+//   1. rowdot dY B^T -> G, kept as bf16 hi / lo parts: rows of s G for the
+//      dX GEMM, transposed planes of G and of XA for the two tokdots
 //   2. tokdot dY^T XA -> dB
 //   3. dequant-GEMM dX with the s G A^T term in its epilogue
 //   4. tokdot X^T G -> dA
@@ -17,6 +17,7 @@
 #include "gemm.hpp"
 #include "kernels.hpp"
 #include "lora.hpp"
+#include "splitk.hpp"
 
 namespace qlora {
 
@@ -53,18 +54,21 @@ int64_t tok_chunk(int64_t T, int64_t C) {
 
 // Backward workspace regions, each 256-byte aligned.
 struct BwdLayout {
-  size_t pg, g, planes, ptok, total;
+  size_t pg, g, planes, ptok, slots, counters, total;
 };
 BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   BwdLayout l{};
   const int64_t RP = rpad(r), TP = round_up(T, 64);
   l.pg = align256((size_t)cdiv(N, row_chunk(T, N)) * T * RP * sizeof(float));
-  l.g = align256((size_t)T * r * sizeof(float));
+  l.g = align256((size_t)T * RP * sizeof(uint16_t));
   l.planes = align256((size_t)RP * TP * sizeof(uint16_t));
   const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * RP * N * sizeof(float);
   const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * RP * K * sizeof(float);
   l.ptok = align256(pdb > pda ? pdb : pda);
-  l.total = l.pg + l.g + 4 * l.planes + l.ptok;
+  const DxGrid dg = dx_grid(T, K, N);
+  l.slots = dg.S > 1 ? align256((size_t)dg.tiles * dg.S * kSplitSlotFloats * sizeof(float)) : 0;
+  l.counters = align256((size_t)dg.tiles * sizeof(int));
+  l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok + l.slots + l.counters;
   return l;
 }
 }  // namespace
@@ -113,24 +117,33 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   const BwdLayout l = bwd_layout(a.T, a.K, a.N, a.r);
   char* w = reinterpret_cast<char*>(ws);
   float* Pg = reinterpret_cast<float*>(w);
-  float* G = reinterpret_cast<float*>(w + l.pg);
-  uint16_t* Gth = reinterpret_cast<uint16_t*>(w + l.pg + l.g);
-  uint16_t* Gtl = reinterpret_cast<uint16_t*>(w + l.pg + l.g + l.planes);
-  uint16_t* XAth = reinterpret_cast<uint16_t*>(w + l.pg + l.g + 2 * l.planes);
-  uint16_t* XAtl = reinterpret_cast<uint16_t*>(w + l.pg + l.g + 3 * l.planes);
-  float* Ptok = reinterpret_cast<float*>(w + l.pg + l.g + 4 * l.planes);
+  uint16_t* Gh = reinterpret_cast<uint16_t*>(w + l.pg);
+  uint16_t* Gl = reinterpret_cast<uint16_t*>(w + l.pg + l.g);
+  char* w2 = w + l.pg + 2 * l.g;
+  uint16_t* Gth = reinterpret_cast<uint16_t*>(w2);
+  uint16_t* Gtl = reinterpret_cast<uint16_t*>(w2 + l.planes);
+  uint16_t* XAth = reinterpret_cast<uint16_t*>(w2 + 2 * l.planes);
+  uint16_t* XAtl = reinterpret_cast<uint16_t*>(w2 + 3 * l.planes);
+  float* Ptok = reinterpret_cast<float*>(w2 + 4 * l.planes);
+  float* slots = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok);
+  int* counters = reinterpret_cast<int*>(w2 + 4 * l.planes + l.ptok + l.slots);
+  const DxGrid dg = dx_grid(a.T, a.K, a.N);
   const int64_t TP = round_up(a.T, 64);
 
-  // G = dY B^T (fp32 for the dX epilogue, transposed hi / lo planes for dA),
-  // plus the transposed hi / lo planes of XA for dB.
+  // G = dY B^T as the bf16 hi / lo rows of s G (the dX GEMM's adapter step)
+  // and as transposed hi / lo planes (dA), plus the planes of XA (dB).
   RowdotOut o{};
-  o.f32 = G;
+  o.row_hi = Gh;
+  o.row_lo = Gl;
+  o.scale_row = a.s;
   o.t_hi = Gth;
   o.t_lo = Gtl;
   o.TP = TP;
   o.side = XA;
   o.side_hi = XAth;
   o.side_lo = XAtl;
+  o.zero = counters;  // the dX GEMM's split tickets
+  o.nzero = dg.tiles;
   hipError_t e = launch_rowdot(dY, a.B, /*v_lr=*/false, Pg, o, a.T, a.N, a.r, row_chunk(a.T, a.N), s);
   if (e != hipSuccess) return e;
   e = launch_tokdot(dY, XAth, XAtl, TP, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*m_major=*/false, s);
@@ -141,13 +154,17 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   p.q8 = a.q8;
   p.s2 = a.s2;
   p.A = a.A;
-  p.G = G;
+  p.Gh = Gh;
+  p.Gl = Gl;
   p.dX = dX;
   p.T = a.T;
   p.K = a.K;
   p.N = a.N;
   p.r = a.r;
-  p.s = a.s;
+  p.RP = (int)rpad(a.r);
+  p.slots = slots;
+  p.counters = counters;
+  p.S = dg.S;
   e = launch_gemm_dx(p, cb, s);
   if (e != hipSuccess) return e;
   return launch_tokdot(X, Gth, Gtl, TP, Ptok, dA, a.T, a.K, a.r, tok_chunk(a.T, a.K), a.s, /*m_major=*/true, s);

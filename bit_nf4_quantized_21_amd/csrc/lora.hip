@@ -172,6 +172,8 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int jb = blockIdx.y;
   const bool want_t = o.t_hi != nullptr, want_side = o.side != nullptr;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < o.nzero; i += 256) o.zero[i] = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int q = threadIdx.x + 256 * k;

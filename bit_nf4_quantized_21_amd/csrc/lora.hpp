@@ -19,6 +19,8 @@ struct RowdotOut {
   const float* side;     // optional extra [T][r] fp32 input, transposed and split
   uint16_t* side_hi;     // into [RP][TP] hi / lo planes
   uint16_t* side_lo;
+  int* zero;             // optional ints set to zero (counters of a later kernel)
+  int64_t nzero;
 };
 
 // out[T][r] = M[T,L] V  with V = A[L,r] (v_lr) or B[r,L]^T.  P is scratch of
