@@ -19,7 +19,10 @@ struct FwdGemmParams {
   int64_t T, K, N;
   int r;
   float s;
-  int tiles_n, tiles_m, per_xcd;  // filled by the launcher
+  float* slots;          // split partials: tiles * S * 65536 floats (S > 1)
+  int* counters;         // one per tile, zero on entry, left zero
+  int S;                 // contraction slices per tile (GEMM only)
+  int tiles_n, tiles_m, per_xcd, steps_per;  // filled by the launcher
 };
 
 struct DxGemmParams {
@@ -50,5 +53,6 @@ struct DxGrid {
   int S;
 };
 DxGrid dx_grid(int64_t T, int64_t K, int64_t N);
+DxGrid fwd_grid(int64_t T, int64_t K, int64_t N);
 
 }  // namespace qlora

@@ -41,6 +41,7 @@
 //    re-read from there by every n-tile.
 #include "common.hpp"
 #include "gemm.hpp"
+#include "splitk.hpp"
 #include "timing.hpp"
 
 namespace qlora {
@@ -63,10 +64,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // Workgroups are dispatched round-robin over the 8 XCDs; tiles are ordered
   // token-tile-major and each XCD takes a contiguous run of them, so the X
   // tile (the operand re-read by every n-tile) stays in that XCD's L2.
+  // Items are (tile, contraction slice) pairs, slices of a tile adjacent.
   const int bid = blockIdx.x;
-  const int tile = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (tile >= p.tiles_n * p.tiles_m) return;  // uniform per workgroup, before any barrier
-  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+  const int item = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (item >= p.tiles_n * p.tiles_m * p.S) return;  // uniform per workgroup, before any barrier
+  const int tile = __builtin_amdgcn_readfirstlane(item / p.S), sidx = __builtin_amdgcn_readfirstlane(item % p.S);
+  const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
 
   if (tid < 16) lut[tid] = cb.c[tid];
 
@@ -75,6 +78,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int64_t n0 = (int64_t)tn * kTileN, m0 = (int64_t)tm * kTileM;
   const int64_t K2 = K / 2, bpr = K / 64;
   const int nk = (int)(K / 64);
+  const int kbeg = sidx * p.steps_per;
+  const int kend = kbeg + p.steps_per < nk ? kbeg + p.steps_per : nk;
+  auto clampk = [&](int k) { return k < nk ? k : nk - 1; };  // past the end: redundant, in bounds
 
   // Buffer views of this tile's rows: reads past the last row return zero.
   const rsrc_t rx = make_rsrc(p.X + m0 * K, (T - m0) * K * 2);
@@ -157,12 +163,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
 
   // Prologue: X(0), X(1) in the ring, X(2) in registers, W(0) decoded,
   // codes(1) in flight.
-  load_w(0, cA, qA, sA);
-  load_x(0, xr);
+  load_w(kbeg, cA, qA, sA);
+  load_x(kbeg, xr);
   store_x(0, xr);
-  load_x(nk > 1 ? 1 : 0, xr);
+  load_x(clampk(kbeg + 1), xr);
   store_x(1, xr);
-  load_x(nk > 2 ? 2 : 0, xr);
+  load_x(clampk(kbeg + 2), xr);
   __syncthreads();  // lut and X(0..1) visible to every wave
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     lut8(cA[g][3], fp[g]);  // chunk 3 of W(0) is packed in the first substep, like every step's
     scp[g] = sc;
   }
-  load_w(nk > 1 ? 1 : 0, cA, qA, sA);
+  load_w(clampk(kbeg + 1), cA, qA, sA);
   read_x(0, 0, xa);
 
   // Substep S: MFMAs on (wc[.][S], XCUR); X of the next substep -> XNXT;
@@ -263,8 +269,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // Whole groups of six steps loop; the remainder runs once after the loop,
   // so the loop back-edge is reached from one path only and the wait counts
   // at its top stay exact.
-  int kb = 0;
-  for (; kb + 6 <= nk; kb += 6) {
+  int kb = kbeg;
+  for (; kb + 6 <= kend; kb += 6) {
     QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
     QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
     QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
@@ -272,12 +278,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
     QLORA_FWD_STEP(kb + 5, 2, 0, 1, cB, qB, sB, cA, qA, sA)
   }
-  if (kb < nk) {
+  if (kb < kend) {
     QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
-    if (kb + 1 < nk) QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
-    if (kb + 2 < nk) QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
-    if (kb + 3 < nk) QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
-    if (kb + 4 < nk) QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
+    if (kb + 1 < kend) QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
+    if (kb + 2 < kend) QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
+    if (kb + 3 < kend) QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
+    if (kb + 4 < kend) QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
   }
 #undef QLORA_FWD_STEP
 #undef QLORA_FWD_SUBSTEP
@@ -286,7 +292,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // LoRA up-projection as one extra K-step of width r: A = B^T (rows n),
   // B operand = s * XA (columns m) as a bf16 hi + lo pair, so the fp32 XA
   // keeps ~16 significant bits even where the adapter term dominates Y.
-  const int r = p.r;
+  // Slice 0 carries the adapter term.
+  const int r = sidx == 0 ? p.r : 0;
   for (int c16 = 0; c16 < r; c16 += 16) {
     const int j0 = c16 + 8 * h;
     const bool jv = j0 < r;  // r % 8 == 0: the 8-group is whole or absent
@@ -321,6 +328,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     }
   }
 
+  if (p.S > 1) {
+    __syncthreads();  // every wave is done with LDS; its first word holds the ticket
+    if (!splitk_combine(acc, p.slots + (int64_t)tile * p.S * kSplitSlotFloats, p.counters + tile, p.S, sidx,
+                        reinterpret_cast<int*>(smem + 64)))
+      return;
+  }
+
   // D[n][m]: lane holds column m and rows n = 8*q4 + 4h + (0..3) of each 32x32 tile.
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi) {
@@ -341,11 +355,20 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   }
 }
 
+DxGrid fwd_grid(int64_t T, int64_t K, int64_t N) {
+  DxGrid g;
+  g.tiles = ((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
+  g.S = choose_split(g.tiles, K / 64);
+  return g;
+}
+
 hipError_t launch_gemm_fwd(const FwdGemmParams& p0, const Codebook& cb, hipStream_t s) {
   FwdGemmParams p = p0;
   p.tiles_n = (int)((p.N + kTileN - 1) / kTileN);
   p.tiles_m = (int)((p.T + kTileM - 1) / kTileM);
-  const int total = p.tiles_n * p.tiles_m;
+  const int64_t nk = p.K / 64;
+  p.steps_per = (int)((nk + p.S - 1) / p.S);
+  const int total = p.tiles_n * p.tiles_m * p.S;
   p.per_xcd = (total + 7) / 8;
   {
     KernelTimer kt_("gemm_fwd_kernel", s);

@@ -73,9 +73,27 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
 }
 }  // namespace
 
-size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t /*N*/, int32_t r) {
+// Forward workspace: rowdot partials, then (GEMM path) split partials and
+// tile counters.
+struct FwdLayout {
+  size_t p, slots, counters, total;
+  DxGrid g;
+};
+FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
+  FwdLayout l{};
+  l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
+  if (T > kGemvMaxT) {
+    l.g = fwd_grid(T, K, N);
+    l.slots = l.g.S > 1 ? align256((size_t)l.g.tiles * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
+    l.counters = align256((size_t)l.g.tiles * sizeof(int));
+  }
+  l.total = l.p + l.slots + l.counters;
+  return l;
+}
+
+size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
   if (T <= 0) return 0;
-  return align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
+  return fwd_layout(T, K, N, r).total;
 }
 
 size_t bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
@@ -86,9 +104,15 @@ size_t bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
 hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint16_t* X, uint16_t* Y, float* XA,
                              void* ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  float* P = reinterpret_cast<float*>(ws);
+  const FwdLayout l = fwd_layout(a.T, a.K, a.N, a.r);
+  char* w = reinterpret_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(w);
   RowdotOut o{};
   o.f32 = XA;
+  if (a.T > kGemvMaxT) {
+    o.zero = reinterpret_cast<int*>(w + l.p + l.slots);  // the GEMM's split tickets
+    o.nzero = l.g.tiles;
+  }
   hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
   if (e != hipSuccess) return e;
   FwdGemmParams p{};
@@ -104,6 +128,9 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   p.N = a.N;
   p.r = a.r;
   p.s = a.s;
+  p.slots = reinterpret_cast<float*>(w + l.p);
+  p.counters = reinterpret_cast<int*>(w + l.p + l.slots);
+  p.S = a.T > kGemvMaxT ? l.g.S : 1;
   return a.T <= kGemvMaxT ? launch_gemv_fwd(p, cb, s) : launch_gemm_fwd(p, cb, s);
 }
 

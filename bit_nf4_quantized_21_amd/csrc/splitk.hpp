@@ -62,23 +62,16 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
 }
 
 // Number of slices for a grid of `tiles` tiles of `steps` contraction steps
-// on 256 compute units: fewest tile rounds per step, charging each extra
-// slice for its partial-sum traffic.
+// on 256 compute units: split only to fill otherwise idle units (measured on
+// the 7B MLP shapes, splitting a grid that already covers the chip costs more
+// in partial-sum traffic and per-workgroup start-up than the shorter last
+// round saves).
 inline int choose_split(int64_t tiles, int64_t steps) {
   int best = 1;
-  double best_cost = 1e30;
-  for (int S = 1; S <= 4; ++S) {
-    if (S > steps) break;
+  for (int S = 2; S <= 4; ++S) {
+    if (tiles * S > 256 || S > steps) break;
     if ((steps + S - 1) / S * (S - 1) >= steps) continue;  // no empty slice
-    const double rounds = (double)((tiles * S + 255) / 256);
-    const double per = (double)((steps + S - 1) / S);
-    // ~1.5 x 256 KiB of traffic per slice at ~5 TB/s, in units of a ~2.5 us step
-    const double extra = S > 1 ? (double)tiles * S * 0.4e6 / 5e12 / 2.5e-6 : 0.0;
-    const double cost = rounds * per + extra;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = S;
-    }
+    best = S;
   }
   return best;
 }
