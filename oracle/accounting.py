@@ -9,7 +9,7 @@ These connect the stored format to the figures the pages print:
     instead of 100*500 = 50000, and a rank-8 LoRA for 7B LLaMA is about 8 MB
     (LoRA tutorial, section on parameter efficiency).
 
-Readings (DESIGN.md): the 780 GB figure is read as 16-bit weights and
+Readings: the 780 GB figure is read as 16-bit weights and
 gradients plus two fp32 Adam moments (2 + 2 + 8 bytes per parameter); the
 8 MB figure as adapters on the q and v projections of the 32 layers of
 LLaMA-7B (hidden 4096) stored in 16 bits.

@@ -3,7 +3,7 @@ TEST INFRASTRUCTURE ONLY.
 
 The pages state that NF4 gives better results than 4-bit integers and 4-bit
 floats (news write-up, innovations list and the NF4-vs-FP4 section; project
-page, core innovations).  Reading R11 (DESIGN.md) fixes the comparison types:
+page, core innovations).  Reading R11 fixes the comparison types:
   * Int4, symmetric absmax with the 15 levels k/7, k = -7..7 (and the 16-level
     two's-complement variant k/8, k = -8..7);
   * FP4 as E2M1 with magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6} / 6 and a sign;

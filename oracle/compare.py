@@ -1,7 +1,7 @@
 """Tolerance rule for bf16 outputs and gradients.  TEST INFRASTRUCTURE ONLY.
 
 The bar (relative Frobenius error <= 5e-3, max elementwise error <= 1e-2 of
-the output RMS) is the one stated for this layer.  Reading R10 (DESIGN.md):
+the output RMS) is the one stated for this layer.  Reading R10:
 the elementwise bound is taken as
 
     |got - ref| <= max_tol * RMS(ref) + 0.5 * ulp_bf16(max(|ref|, |got|))

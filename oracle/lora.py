@@ -10,7 +10,7 @@ What the pages fix:
     r x B; W stays frozen and only W_A and W_B are trained; a scale alpha
     multiplies the adapter output (section on the rank and alpha).
 
-Readings (repeated in DESIGN.md):
+Readings:
   R7  Row-vector convention with tokens as rows: X [T,K], dequantized weight
       W' [N,K], adapter A [K,r] and B [r,N], scale s = alpha / r (computed in
       fp32, exact in every configuration used here):

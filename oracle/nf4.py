@@ -11,7 +11,7 @@ What the pages fix:
   * Weights are computed in bf16 (QLoRA project page, configuration example:
     4-bit load, 'nf4', double quantization on, bf16 compute dtype).
 
-Readings taken where the pages are silent (each is repeated in the design doc):
+Readings taken where the pages are silent:
   R1  Codebook: 7 negative values, an exact zero and 8 positive values, each
       the standard-normal quantile at probabilities equally spaced on
       [1/2, p_max] (8 steps on the positive side, 7 on the negative side),
