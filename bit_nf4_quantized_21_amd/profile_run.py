@@ -113,10 +113,11 @@ def run(steps):
 
 
 def short_name(name):
-    n = name.split("(")[0].strip()
+    n = name.replace("(anonymous namespace)::", "").strip()
     if n.startswith("void "):
         n = n[5:]
-    return n.split("<")[0].split("::")[-1]
+    cut = min([i for i in (n.find("("), n.find("<")) if i >= 0] or [len(n)])
+    return n[:cut].split("::")[-1]
 
 
 def read_counter(d, counter):
