@@ -14,10 +14,12 @@ struct FwdGemmParams {
   const uint8_t* q8;     // [N*K/64]
   const float* s2;       // [ceil(N*K/64/256)]
   const uint16_t* B;     // [r,N] bf16
-  const float* XA;       // [T,r] fp32
+  const float* XA;       // [T,r] fp32 (GEMV path)
+  const uint16_t* XAh;   // [T,RP] bf16 hi part of s*XA, zero past r (GEMM path)
+  const uint16_t* XAl;   // [T,RP] bf16 lo part
   uint16_t* Y;           // [T,N] bf16
   int64_t T, K, N;
-  int r;
+  int r, RP;             // RP = r rounded up to 64
   float s;
   float* slots;          // split partials: tiles * S * 65536 floats (S > 1)
   int* counters;         // one per tile, zero on entry, left zero

@@ -276,31 +276,40 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
 #undef QLORA_DX_DECODE
   // Every buffer is free after the last step's barrier.
 
-  // Adapter term: A[k][j] (rows k) against the hi and lo planes of s G
-  // (rows t), 64 j per pass.
-  // Slice 0 carries the adapter term.
+  // Adapter term: A[k][j] (rows k) against the hi and lo rows of s G
+  // (rows t), 64 j per pass, carried by slice 0.  The three tiles are copied
+  // by buffer-to-LDS loads straight into the swizzled layout: wave w fills
+  // rows [64w, 64w+64), 8 rows per instruction, lane l the physical chunk
+  // l % 8 of row l / 8 with the logical chunk it holds; chunks past r read
+  // zero through an out-of-range offset.
   const int r = p.r;
-  for (int jb = 0; jb < (sidx == 0 ? p.RP : 0); jb += 64) {
-    const int jj = jb + 8 * xc;
-    u32x4 va[8], vh[8], vl[8];
+  if (sidx == 0) {
+    const rsrc_t ra = make_rsrc(p.A + k0 * r, (K - k0) * r * 2);
+    const rsrc_t rgh = make_rsrc(p.Gh + t0 * p.RP, (T - t0) * p.RP * 2);
+    const rsrc_t rgl = make_rsrc(p.Gl + t0 * p.RP, (T - t0) * p.RP * 2);
+    const int drow = lane >> 3, dphys = lane & 7;
+    for (int jb = 0; jb < p.RP; jb += 64) {
+      __syncthreads();  // every wave is done with the buffers
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t k = k0 + xr + 32 * i, t = t0 + xr + 32 * i;
-      va[i] = (k < K && jj < r) ? *reinterpret_cast<const u32x4*>(p.A + k * r + jj) : u32x4{0u, 0u, 0u, 0u};
-      vh[i] = t < T ? *reinterpret_cast<const u32x4*>(p.Gh + t * p.RP + jj) : u32x4{0u, 0u, 0u, 0u};
-      vl[i] = t < T ? *reinterpret_cast<const u32x4*>(p.Gl + t * p.RP + jj) : u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();  // every wave is done with the buffers
-    store_rows(kW0, va);
-    store_rows(kD0, vh);
-    store_rows(kD1, vl);
-    __syncthreads();
+      for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + drow;
+        const int lchunk = dphys ^ (((row >> 1) ^ (row >> 4)) & 7);
+        const int jj = jb + 8 * lchunk;
+        const uint32_t ao = jj < r ? (uint32_t)(row * r * 2 + jj * 2) : 0x7FFFFFF0u;
+        const uint32_t go = (uint32_t)(row * p.RP * 2 + jj * 2);
+        buf_load16_to_lds(ra, smem + kW0 + (64 * wave + 8 * i) * 128, ao);
+        buf_load16_to_lds(rgh, smem + kD0 + (64 * wave + 8 * i) * 128, go);
+        buf_load16_to_lds(rgl, smem + kD1 + (64 * wave + 8 * i) * 128, go);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      read_ops(kW0, kD0, s, oa0, ob0);
-      QLORA_DX_MFMA(oa0, ob0)
-      read_ops(kW0, kD1, s, oa1, ob1);
-      QLORA_DX_MFMA(oa1, ob1)
+      for (int s = 0; s < 4; ++s) {
+        read_ops(kW0, kD0, s, oa0, ob0);
+        QLORA_DX_MFMA(oa0, ob0)
+        read_ops(kW0, kD1, s, oa1, ob1);
+        QLORA_DX_MFMA(oa1, ob1)
+      }
     }
   }
 #undef QLORA_DX_MFMA

@@ -289,47 +289,68 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
 #undef QLORA_FWD_SUBSTEP
 #undef QLORA_FWD_SUBSTEP3
 
-  // LoRA up-projection as one extra K-step of width r: A = B^T (rows n),
-  // B operand = s * XA (columns m) as a bf16 hi + lo pair, so the fp32 XA
-  // keeps ~16 significant bits even where the adapter term dominates Y.
-  // Slice 0 carries the adapter term.
-  const int r = sidx == 0 ? p.r : 0;
-  for (int c16 = 0; c16 < r; c16 += 16) {
-    const int j0 = c16 + 8 * h;
-    const bool jv = j0 < r;  // r % 8 == 0: the 8-group is whole or absent
-    bf16x8 aop[2];
+  // LoRA up-projection as two more K-steps of 64 j per pass: A operand =
+  // B^T (rows n), B operand = the bf16 hi and lo rows of s XA (rows m), so
+  // the fp32 XA keeps ~16 significant bits even where the adapter term
+  // dominates Y.  Slice 0 carries it.  The B^T tile is built in LDS by
+  // loading 8 rows j x 8 columns n per lane and transposing them in
+  // registers; the hi / lo tiles are copied by buffer-to-LDS loads straight
+  // into the swizzled X-stage layout.
+  if (sidx == 0) {
+    const int r = p.r;
+    const rsrc_t rh = make_rsrc(p.XAh + m0 * p.RP, (T - m0) * p.RP * 2);
+    const rsrc_t rl = make_rsrc(p.XAl + m0 * p.RP, (T - m0) * p.RP * 2);
+    const int bjg = tid & 7, bng = tid >> 3;  // lane's 8 j and 8 n of the B tile
+    const int64_t bn = n0 + 8 * bng;
+    const int drow = lane >> 3, dphys = lane & 7;
+    for (int jb = 0; jb < p.RP; jb += 64) {
+      u32x4 brow[8];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      uint32_t e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = (nval[g] && jv) ? p.B[(int64_t)(j0 + i) * N + n0 + nl[g]] : 0u;
-      aop[g] = as_bf16x8(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
-    }
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-      const int64_t m = m0 + 32 * mi + ml;
-      float v[8];
-      if (jv && m < T) {
-        const float4 a = *reinterpret_cast<const float4*>(p.XA + m * r + j0);
-        const float4 b = *reinterpret_cast<const float4*>(p.XA + m * r + j0 + 4);
-        v[0] = a.x * p.s; v[1] = a.y * p.s; v[2] = a.z * p.s; v[3] = a.w * p.s;
-        v[4] = b.x * p.s; v[5] = b.y * p.s; v[6] = b.z * p.s; v[7] = b.w * p.s;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) {
+        const int j = jb + 8 * bjg + i;
+        brow[i] = (j < r && bn < N) ? *reinterpret_cast<const u32x4*>(p.B + (int64_t)j * N + bn)
+                                    : u32x4{0u, 0u, 0u, 0u};
       }
-      bf16x8 bhi, blo;
-      split_bf16x8(v, bhi, blo);
+      __syncthreads();  // every wave is done with the stages
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        acc[g][mi] = mfma32(aop[g], bhi, acc[g][mi]);
-        acc[g][mi] = mfma32(aop[g], blo, acc[g][mi]);
+      for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + drow;
+        const uint32_t off = (uint32_t)(row * p.RP * 2 + (jb + 8 * (dphys ^ ((row >> 1) & 7))) * 2);
+        buf_load16_to_lds(rh, xring[1] + (64 * wave + 8 * i) * 128, off);
+        buf_load16_to_lds(rl, xring[2] + (64 * wave + 8 * i) * 128, off);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_perm(brow[2 * q + 1][c >> 1], brow[2 * q][c >> 1], sel);
+        const int row = 8 * bng + c;
+        *reinterpret_cast<u32x4*>(xring[0] + row * 128 + ((bjg ^ ((row >> 1) & 7)) << 4)) = v;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 aop[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          aop[g] = *reinterpret_cast<const bf16x8*>(xring[0] + (64 * wave + 32 * g + ml) * 128 + (((4 * h + s) ^ sw) << 4));
+        read_x(1, s, xa);
+        read_x(2, s, xb);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            acc[g][mi] = mfma32(aop[g], xa[mi], acc[g][mi]);
+            acc[g][mi] = mfma32(aop[g], xb[mi], acc[g][mi]);
+          }
       }
     }
   }
 
   if (p.S > 1) {
-    __syncthreads();  // every wave is done with LDS; its first word holds the ticket
+    __syncthreads();  // every wave is done with LDS; word 16 holds the ticket
     if (!splitk_combine(acc, p.slots + (int64_t)tile * p.S * kSplitSlotFloats, p.counters + tile, p.S, sidx,
                         reinterpret_cast<int*>(smem + 64)))
       return;

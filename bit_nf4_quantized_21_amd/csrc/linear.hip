@@ -76,18 +76,19 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
 // Forward workspace: rowdot partials, then (GEMM path) split partials and
 // tile counters.
 struct FwdLayout {
-  size_t p, slots, counters, total;
+  size_t p, xah, slots, counters, total;
   DxGrid g;
 };
 FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   FwdLayout l{};
   l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
   if (T > kGemvMaxT) {
+    l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
     l.g = fwd_grid(T, K, N);
     l.slots = l.g.S > 1 ? align256((size_t)l.g.tiles * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
     l.counters = align256((size_t)l.g.tiles * sizeof(int));
   }
-  l.total = l.p + l.slots + l.counters;
+  l.total = l.p + 2 * l.xah + l.slots + l.counters;
   return l;
 }
 
@@ -109,8 +110,14 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   float* P = reinterpret_cast<float*>(w);
   RowdotOut o{};
   o.f32 = XA;
+  uint16_t* XAh = reinterpret_cast<uint16_t*>(w + l.p);
+  uint16_t* XAl = reinterpret_cast<uint16_t*>(w + l.p + l.xah);
+  char* w2 = w + l.p + 2 * l.xah;
   if (a.T > kGemvMaxT) {
-    o.zero = reinterpret_cast<int*>(w + l.p + l.slots);  // the GEMM's split tickets
+    o.row_hi = XAh;  // s XA as bf16 hi / lo rows for the GEMM's adapter steps
+    o.row_lo = XAl;
+    o.scale_row = a.s;
+    o.zero = reinterpret_cast<int*>(w2 + l.slots);  // the GEMM's split tickets
     o.nzero = l.g.tiles;
   }
   hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
@@ -128,8 +135,11 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   p.N = a.N;
   p.r = a.r;
   p.s = a.s;
-  p.slots = reinterpret_cast<float*>(w + l.p);
-  p.counters = reinterpret_cast<int*>(w + l.p + l.slots);
+  p.XAh = XAh;
+  p.XAl = XAl;
+  p.RP = (int)rpad(a.r);
+  p.slots = reinterpret_cast<float*>(w2);
+  p.counters = reinterpret_cast<int*>(w2 + l.slots);
   p.S = a.T > kGemvMaxT ? l.g.S : 1;
   return a.T <= kGemvMaxT ? launch_gemv_fwd(p, cb, s) : launch_gemm_fwd(p, cb, s);
 }
