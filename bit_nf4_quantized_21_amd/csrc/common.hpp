@@ -120,6 +120,31 @@ __device__ __forceinline__ void buf_load16_to_lds(rsrc_t r, void* lds_block, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_block, 16, (int)off, 0, 0, 0);
 }
 
+// v_bfe_u32 with constant offset / width, kept as one instruction (the
+// compiler otherwise splits some extracts into a shift and a mask).
+template <int OFF, int W>
+__device__ __forceinline__ uint32_t bfe(uint32_t x) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "i"(OFF), "i"(W));
+  return r;
+}
+
+// Codebook values of the 8 codes of a dword, element e = nibble e, from the
+// 16-entry fp32 table at LDS address 0 (`lds` points there): byte q of
+// (x << 2) & 0x3C3C3C3C is 4 * code(2q), of (x >> 2) & 0x3C3C3C3C is
+// 4 * code(2q + 1), so each lookup address is one bitfield extract.
+__device__ __forceinline__ void lut8_lds0(const unsigned char* lds, uint32_t x, float (&f)[8]) {
+  const uint32_t y4 = (x << 2) & 0x3C3C3C3Cu, z4 = (x >> 2) & 0x3C3C3C3Cu;
+  f[0] = *reinterpret_cast<const float*>(lds + bfe<0, 8>(y4));
+  f[1] = *reinterpret_cast<const float*>(lds + bfe<0, 8>(z4));
+  f[2] = *reinterpret_cast<const float*>(lds + bfe<8, 8>(y4));
+  f[3] = *reinterpret_cast<const float*>(lds + bfe<8, 8>(z4));
+  f[4] = *reinterpret_cast<const float*>(lds + bfe<16, 8>(y4));
+  f[5] = *reinterpret_cast<const float*>(lds + bfe<16, 8>(z4));
+  f[6] = *reinterpret_cast<const float*>(lds + bfe<24, 8>(y4));
+  f[7] = *reinterpret_cast<const float*>(lds + bfe<24, 8>(z4));
+}
+
 // Workgroup barrier that waits for this wave's LDS operations only (global
 // loads stay in flight across it).  The memory clobber keeps the compiler
 // from moving memory accesses across the barrier.

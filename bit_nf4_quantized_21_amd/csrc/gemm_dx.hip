@@ -50,14 +50,6 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ (((row >> 1) ^ (row >> 4)) & 7)) << 4));
 }
 
-// v_bfe_u32 with constant offset / width (kept as one instruction).
-template <int OFF, int W>
-__device__ __forceinline__ uint32_t bfe(uint32_t x) {
-  uint32_t r;
-  asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "i"(OFF), "i"(W));
-  return r;
-}
-
 // Codebook values (table at LDS address 0) of nibbles 4 HF .. 4 HF + 3 of a
 // code dword: byte q of (x << 2) & 0x3C3C3C3C is 4 * code(2q), of
 // (x >> 2) & 0x3C3C3C3C is 4 * code(2q + 1).

@@ -121,17 +121,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
     }
   };
-  // Codebook lookups for 8 codes: the byte address of each code's table
-  // entry is a byte of (x << 2) or (x >> 2).
-  const unsigned char* lutb = smem;
-  auto lut8 = [&](uint32_t x, float(&f)[8]) {
-    const uint32_t y4 = (x << 2) & 0x3C3C3C3Cu, z4 = (x >> 2) & 0x3C3C3C3Cu;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f[2 * q] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(y4, 8 * q, 8));
-      f[2 * q + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(z4, 8 * q, 8));
-    }
-  };
+  auto lut8 = [&](uint32_t x, float(&f)[8]) { lut8_lds0(smem, x, f); };
   auto pack8 = [&](const float(&f)[8], float sc) -> bf16x8 {
     return as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
                      pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc));

@@ -16,11 +16,11 @@ constexpr int kSplitSlotFloats = 256 * 256;  // one tile of fp32 partials
 
 // Returns true in the workgroup that must finish the tile (acc then holds the
 // full sum); false in the others, which must exit without storing.  Called by
-// all 256 threads of the workgroup; flag is one int of LDS.
-template <int NA, int NB>
+// all NT threads of the workgroup; flag is one int of LDS.
+template <int NA, int NB, int NT = 256>
 __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __restrict__ slots, int* counter,
                                                int S, int sidx, int* flag) {
-  static_assert(NA * NB * 16 * 256 == kSplitSlotFloats, "tile size");
+  static_assert(NA * NB * 16 * NT == kSplitSlotFloats, "tile size");
   const int tid = threadIdx.x;
   float4* mine = reinterpret_cast<float4*>(slots) + (int64_t)sidx * (kSplitSlotFloats / 4);
 #pragma unroll
@@ -29,7 +29,7 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4)
-        mine[((a * NB + b) * 4 + e4) * 256 + tid] =
+        mine[((a * NB + b) * 4 + e4) * NT + tid] =
             make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]);
   __threadfence();  // this slot is visible device-wide before the ticket
   __syncthreads();
@@ -43,7 +43,7 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t idx = ((a * NB + b) * 4 + e4) * 256 + tid;
+        const int64_t idx = ((a * NB + b) * 4 + e4) * NT + tid;
         const float4 own = make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2],
                                        acc[a][b][4 * e4 + 3]);
         const float4* sl = reinterpret_cast<const float4*>(slots);
