@@ -164,19 +164,22 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
 //   t_hi/lo  [RP][TP] bf16 split of v, transposed (zero outside T x r)
 //   side -> side_hi/lo: the same transposed split of an extra fp32 [T][r]
 //   matrix (XA in the backward pass), since it covers the same tile.
-// Workgroup = a 64 t x 64 j tile; thread q handles 4 consecutive j of one t.
+// Workgroup = a 16 t x 64 j tile; thread q handles 4 consecutive j of one t.
+// The grid covers T rounded up to 64, so the planes are written (with
+// zeros past T) over their whole width TP.
 // ---------------------------------------------------------------------------
+constexpr int kRedRows = 16;
 __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const float* __restrict__ P, int64_t T,
                                                             int r, int RP, int nc) {
-  __shared__ __align__(16) uint16_t tr[4][64 * 72];  // [plane][j][t], t padded to 72
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  constexpr int kPad = kRedRows + 8;
+  __shared__ __align__(16) uint16_t tr[4][64 * kPad];  // [plane][j][t]
+  const int64_t t0 = (int64_t)blockIdx.x * kRedRows;
   const int jb = blockIdx.y;
   const bool want_t = o.t_hi != nullptr, want_side = o.side != nullptr;
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int64_t i = threadIdx.x; i < o.nzero; i += 256) o.zero[i] = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int q = threadIdx.x + 256 * k;
+  {
+    const int q = threadIdx.x;
     const int t = q >> 4, j = 64 * jb + 4 * (q & 15);
     const int64_t tg = t0 + t;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -207,8 +210,8 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
       for (int e = 0; e < 4; ++e) {
         const uint32_t h = pack_bf16x2(vv[e], 0.f) & 0xFFFFu;
         const uint32_t l = pack_bf16x2(vv[e] - __uint_as_float(h << 16), 0.f) & 0xFFFFu;
-        tr[0][(j - 64 * jb + e) * 72 + t] = (uint16_t)h;
-        tr[1][(j - 64 * jb + e) * 72 + t] = (uint16_t)l;
+        tr[0][(j - 64 * jb + e) * kPad + t] = (uint16_t)h;
+        tr[1][(j - 64 * jb + e) * kPad + t] = (uint16_t)l;
       }
     }
     if (want_side) {
@@ -219,26 +222,25 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
       for (int e = 0; e < 4; ++e) {
         const uint32_t h = pack_bf16x2(xv[e], 0.f) & 0xFFFFu;
         const uint32_t l = pack_bf16x2(xv[e] - __uint_as_float(h << 16), 0.f) & 0xFFFFu;
-        tr[2][(j - 64 * jb + e) * 72 + t] = (uint16_t)h;
-        tr[3][(j - 64 * jb + e) * 72 + t] = (uint16_t)l;
+        tr[2][(j - 64 * jb + e) * kPad + t] = (uint16_t)h;
+        tr[3][(j - 64 * jb + e) * kPad + t] = (uint16_t)l;
       }
     }
   }
   if (!want_t && !want_side) return;  // uniform per workgroup
   __syncthreads();
-  // Transposed planes: thread q writes 8 consecutive t of row j.
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int j = q >> 3, t8 = 8 * (q & 7);
+  // Transposed planes: thread q < 128 writes 8 consecutive t of row j.
+  if (threadIdx.x < 64 * kRedRows / 8) {
+    const int q = threadIdx.x;
+    const int j = q / (kRedRows / 8), t8 = 8 * (q % (kRedRows / 8));
     const int64_t off = (int64_t)(64 * jb + j) * o.TP + t0 + t8;
     if (want_t) {
-      *reinterpret_cast<u32x4*>(o.t_hi + off) = *reinterpret_cast<const u32x4*>(&tr[0][j * 72 + t8]);
-      *reinterpret_cast<u32x4*>(o.t_lo + off) = *reinterpret_cast<const u32x4*>(&tr[1][j * 72 + t8]);
+      *reinterpret_cast<u32x4*>(o.t_hi + off) = *reinterpret_cast<const u32x4*>(&tr[0][j * kPad + t8]);
+      *reinterpret_cast<u32x4*>(o.t_lo + off) = *reinterpret_cast<const u32x4*>(&tr[1][j * kPad + t8]);
     }
     if (want_side) {
-      *reinterpret_cast<u32x4*>(o.side_hi + off) = *reinterpret_cast<const u32x4*>(&tr[2][j * 72 + t8]);
-      *reinterpret_cast<u32x4*>(o.side_lo + off) = *reinterpret_cast<const u32x4*>(&tr[3][j * 72 + t8]);
+      *reinterpret_cast<u32x4*>(o.side_hi + off) = *reinterpret_cast<const u32x4*>(&tr[2][j * kPad + t8]);
+      *reinterpret_cast<u32x4*>(o.side_lo + off) = *reinterpret_cast<const u32x4*>(&tr[3][j * kPad + t8]);
     }
   }
 }
@@ -346,53 +348,45 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
 }
 
 // out = bf16(s * sum over chunks of P[c][j][m]), stored [j][m] (dB: [r,N]) or
-// [m][j] (dA: [K,r]).  Workgroup = a 64 j x 64 m tile.
+// [m][j] (dA: [K,r]).  Workgroup = a 64 j x 16 m tile; thread q handles 4
+// consecutive m of one j.
 __global__ __launch_bounds__(256) void tokdot_reduce_kernel(const float* __restrict__ P, uint16_t* __restrict__ out,
                                                             int64_t C, int r, int RP, int nc, float s,
                                                             int m_major) {
-  __shared__ __align__(16) uint16_t tr[64 * 72];  // [m][j], j padded to 72
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  __shared__ __align__(16) uint16_t tr[16 * 72];  // [m][j], j padded to 72
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
   const int jb = blockIdx.y;
+  const int q = threadIdx.x;
+  const int j = q >> 2, m4 = 4 * (q & 3);
+  const int jg = 64 * jb + j;
+  const int64_t mg = m0 + m4;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (jg < r && mg < C) {
+    float4 part[8];
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+      const int n = nc - c0 < 8 ? nc - c0 : 8;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int j = q >> 4, m4 = 4 * (q & 15);
-    const int jg = 64 * jb + j;
-    const int64_t mg = m0 + m4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (jg < r && mg < C) {
-      float4 part[8];
-      for (int c0 = 0; c0 < nc; c0 += 8) {
-        const int n = nc - c0 < 8 ? nc - c0 : 8;
+      for (int c = 0; c < 8; ++c)
+        if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * RP + jg) * C + mg);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * RP + jg) * C + mg);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
-      }
-    }
-    const uint32_t p0 = pack_bf16x2(v.x * s, v.y * s), p1 = pack_bf16x2(v.z * s, v.w * s);
-    if (!m_major) {
-      if (jg < r && mg < C) *reinterpret_cast<uint2*>(out + (int64_t)jg * C + mg) = make_uint2(p0, p1);
-    } else {
-      tr[(m4 + 0) * 72 + j] = (uint16_t)(p0 & 0xFFFFu);
-      tr[(m4 + 1) * 72 + j] = (uint16_t)(p0 >> 16);
-      tr[(m4 + 2) * 72 + j] = (uint16_t)(p1 & 0xFFFFu);
-      tr[(m4 + 3) * 72 + j] = (uint16_t)(p1 >> 16);
+      for (int c = 0; c < 8; ++c)
+        if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
     }
   }
-  if (!m_major) return;  // uniform per launch
+  const uint32_t p0 = pack_bf16x2(v.x * s, v.y * s), p1 = pack_bf16x2(v.z * s, v.w * s);
+  if (!m_major) {
+    if (jg < r && mg < C) *reinterpret_cast<uint2*>(out + (int64_t)jg * C + mg) = make_uint2(p0, p1);
+    return;  // uniform per launch
+  }
+  tr[(m4 + 0) * 72 + j] = (uint16_t)(p0 & 0xFFFFu);
+  tr[(m4 + 1) * 72 + j] = (uint16_t)(p0 >> 16);
+  tr[(m4 + 2) * 72 + j] = (uint16_t)(p1 & 0xFFFFu);
+  tr[(m4 + 3) * 72 + j] = (uint16_t)(p1 >> 16);
   __syncthreads();
   // Thread q writes 4 consecutive j of row m.
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int mm = q >> 4, j4 = 4 * (q & 15);
-    const int jg = 64 * jb + j4;
-    if (m0 + mm < C && jg < r)
-      *reinterpret_cast<uint2*>(out + (m0 + mm) * r + jg) = *reinterpret_cast<const uint2*>(&tr[mm * 72 + j4]);
-  }
+  const int mm = q >> 4, j4 = 4 * (q & 15);
+  if (m0 + mm < C && 64 * jb + j4 < r)
+    *reinterpret_cast<uint2*>(out + (m0 + mm) * r + 64 * jb + j4) = *reinterpret_cast<const uint2*>(&tr[mm * 72 + j4]);
 }
 
 // Zero-fill (used for dA / dB when there are no tokens).
@@ -424,7 +418,8 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float*
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("rowdot_reduce_kernel", s);
-    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)cdiv(T, 64), (unsigned)JB), dim3(256), 0, s, o, P, T, r,
+    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)(cdiv(T, 64) * (64 / kRedRows)), (unsigned)JB), dim3(256),
+                       0, s, o, P, T, r,
                        64 * JB, (int)nc);
   }
   return hipGetLastError();
@@ -445,7 +440,7 @@ hipError_t launch_tokdot(const uint16_t* M, const uint16_t* Sh, const uint16_t* 
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("tokdot_reduce_kernel", s);
-    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(r, 64)), dim3(256), 0, s, P,
+    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)cdiv(C, 16), (unsigned)cdiv(r, 64)), dim3(256), 0, s, P,
                        out, C, r, 16 * JT, (int)nc, scale, m_major ? 1 : 0);
   }
   return hipGetLastError();
