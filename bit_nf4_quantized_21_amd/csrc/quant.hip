@@ -8,9 +8,12 @@
 //
 // All three kernels are HBM-bound streams.  The quantizer gives each 64-weight
 // block to 16 lanes (one 16-byte load per lane, a 4-step shuffle max for the
-// absmax) and decides every code exactly with fp64 products against the fp64
-// midpoints of the codebook; the double quantizer gives each group of 256
+// absmax), four blocks per lane group with their loads issued together, and
+// decides every code exactly with fp64 products against the fp64 midpoints
+// of the codebook; the double quantizer gives each group of 256
 // constants to one wavefront.
+#include <cmath>
+
 #include "common.hpp"
 #include "timing.hpp"
 #include "kernels.hpp"
@@ -29,40 +32,136 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double a64, const double* 
   return a64 == 0.0 ? 7u : c;
 }
 
+// Each 16-lane group quantizes kQGroupBlocks consecutive blocks; the loads of
+// all of them are issued before any is used, so a wave keeps 4 KiB of the
+// weight stream in flight.
+constexpr int kQGroupBlocks = 4;
+constexpr int kBins = 128;             // uniform bins of w / absmax over [-1, 1]
+constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
+
+// Nearest code by bins: every bin of width 2/kBins holds at most one decision
+// boundary m_j, none within 1e-5 of a bin edge (checked on the host), so the
+// bin of the fp32 estimate x = w * (1/absmax) (error < 1e-6) contains x's
+// true position or is a neighbour separated from it by no boundary.  The code
+// is the number of boundaries below the bin plus the exact fp64 decision
+// w > absmax * m_j for the bin's own boundary (m = +inf when it has none).
 __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax, Midpoints mp) {
-  const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l16 = threadIdx.x & 15;
-  if (blk >= nb) return;  // whole 16-lane groups leave together
-  const int64_t e0 = blk * kBlock + l16 * 4;
-  const bool full = blk * kBlock + kBlock <= n;
-  float v[4];
-  if (full) {
-    float4 x = *reinterpret_cast<const float4*>(W + e0);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  } else {
+  __shared__ double s_thr[kBins];
+  __shared__ uint32_t s_lo[kBins];
+  if (threadIdx.x < kBins) {
+    const double lo = -1.0 + threadIdx.x * (2.0 / kBins), hi = lo + 2.0 / kBins;
+    uint32_t cnt = 0;
+    double thr = __builtin_inf();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+    for (int j = 0; j < 15; ++j) {
+      if (mp.m[j] < lo) cnt += 1;
+      else if (mp.m[j] < hi) thr = mp.m[j];
+    }
+    s_thr[threadIdx.x] = thr;
+    s_lo[threadIdx.x] = cnt;
   }
-  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  __syncthreads();
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * kQGroupBlocks;
+  const int l16 = threadIdx.x & 15;
+  if (blk0 >= nb) return;  // whole 16-lane groups leave together (after the barrier)
+  float v[kQGroupBlocks][4];
 #pragma unroll
-  for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
-  if (l16 == 0) absmax[blk] = a;
+  for (int g = 0; g < kQGroupBlocks; ++g) {
+    const int64_t blk = blk0 + g;
+    const int64_t e0 = blk * kBlock + l16 * 4;
+    if (blk * kBlock + kBlock <= n) {
+      const float4 x = *reinterpret_cast<const float4*>(W + e0);
+      v[g][0] = x.x; v[g][1] = x.y; v[g][2] = x.z; v[g][3] = x.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[g][i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < kQGroupBlocks; ++g) {
+    const int64_t blk = blk0 + g;
+    if (blk >= nb) break;  // uniform per 16-lane group
+    const int64_t e0 = blk * kBlock + l16 * 4;
+    float a = fmaxf(fmaxf(fabsf(v[g][0]), fabsf(v[g][1])), fmaxf(fabsf(v[g][2]), fabsf(v[g][3])));
+#pragma unroll
+    for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+    if (l16 == 0) absmax[blk] = a;
 
-  const double a64 = (double)a;
-  double thr[15];
+    const double a64 = (double)a;
+    uint32_t c[4];
+    if (a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> code 7
+      double thr[15];
 #pragma unroll
-  for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
-  uint32_t c0 = nf4_code(v[0], a64, thr), c1 = nf4_code(v[1], a64, thr);
-  uint32_t c2 = nf4_code(v[2], a64, thr), c3 = nf4_code(v[3], a64, thr);
-  uint32_t packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
-  if (full) {
-    *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
-  } else {
-    if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);        // n is even: pairs are whole
-    if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+      for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = nf4_code(v[g][i], a64, thr);
+    } else {
+      const float inv = __builtin_amdgcn_rcpf(a);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int b = (int)((v[g][i] * inv + 1.0f) * (0.5f * kBins));
+        b = b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
+        c[i] = s_lo[b] + (((double)v[g][i] > a64 * s_thr[b]) ? 1u : 0u);
+      }
+    }
+    const uint32_t packed = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
+    if (blk * kBlock + kBlock <= n) {
+      *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
+    } else {
+      if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);  // n is even: pairs are whole
+      if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+    }
+  }
+}
+
+// Exact linear scan over the 15 boundaries (used when the bins above do not
+// separate the boundaries of the codebook in use).
+__global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const float* __restrict__ W, int64_t n,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax, Midpoints mp) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * kQGroupBlocks;
+  const int l16 = threadIdx.x & 15;
+  if (blk0 >= nb) return;  // whole 16-lane groups leave together
+  float v[kQGroupBlocks][4];
+#pragma unroll
+  for (int g = 0; g < kQGroupBlocks; ++g) {
+    const int64_t blk = blk0 + g;
+    const int64_t e0 = blk * kBlock + l16 * 4;
+    if (blk * kBlock + kBlock <= n) {
+      const float4 x = *reinterpret_cast<const float4*>(W + e0);
+      v[g][0] = x.x; v[g][1] = x.y; v[g][2] = x.z; v[g][3] = x.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[g][i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < kQGroupBlocks; ++g) {
+    const int64_t blk = blk0 + g;
+    if (blk >= nb) break;  // uniform per 16-lane group
+    const int64_t e0 = blk * kBlock + l16 * 4;
+    float a = fmaxf(fmaxf(fabsf(v[g][0]), fabsf(v[g][1])), fmaxf(fabsf(v[g][2]), fabsf(v[g][3])));
+#pragma unroll
+    for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+    if (l16 == 0) absmax[blk] = a;
+
+    const double a64 = (double)a;
+    double thr[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
+    const uint32_t c0 = nf4_code(v[g][0], a64, thr), c1 = nf4_code(v[g][1], a64, thr);
+    const uint32_t c2 = nf4_code(v[g][2], a64, thr), c3 = nf4_code(v[g][3], a64, thr);
+    const uint32_t packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
+    if (blk * kBlock + kBlock <= n) {
+      *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
+    } else {
+      if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);  // n is even: pairs are whole
+      if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+    }
   }
 }
 
@@ -162,10 +261,24 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax,
                                const Midpoints& mp, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t grid = (nb + 15) / 16;
+  const int64_t grid = (nb + 16 * kQGroupBlocks - 1) / (16 * kQGroupBlocks);
+  // The bins must hold at most one boundary each, none within 1e-5 of an edge.
+  bool binned = true;
+  for (int b = 0; b < kBins && binned; ++b) {
+    const double lo = -1.0 + b * (2.0 / kBins), hi = lo + 2.0 / kBins;
+    int inside = 0;
+    for (int j = 0; j < 15; ++j) {
+      if (mp.m[j] >= lo && mp.m[j] < hi) ++inside;
+      if (std::fabs(mp.m[j] - lo) < 1e-5 || std::fabs(mp.m[j] - hi) < 1e-5) binned = false;
+    }
+    if (inside > 1) binned = false;
+  }
   {
     KernelTimer kt_("quantize_nf4_kernel", s);
-    hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+    if (binned)
+      hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+    else
+      hipLaunchKernelGGL(quantize_nf4_scan_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
   }
   return hipGetLastError();
 }
