@@ -24,6 +24,18 @@ struct Midpoints {
   double m[15];
 };
 
+// Writes the codebook to lut[0..15] (16-byte aligned) from thread 0 with
+// four vector stores of the kernel argument's values.  No lane-indexed read
+// of the argument is issued: such a read is a memory load that would wait for
+// every load issued before it.
+__device__ __forceinline__ void codebook_to_lds(float* lut, const Codebook& cb, int tid) {
+  if (tid == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<float4*>(lut)[q] = make_float4(cb.c[4 * q], cb.c[4 * q + 1], cb.c[4 * q + 2], cb.c[4 * q + 3]);
+  }
+}
+
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 // `lo` lands in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // built from them must be uniform).
   const int tk = __builtin_amdgcn_readfirstlane(tile / p.tiles_t);
   const int tt = __builtin_amdgcn_readfirstlane(tile % p.tiles_t);
-  if (tid < 16) reinterpret_cast<float*>(smem)[tid] = cb.c[tid];
+  codebook_to_lds(reinterpret_cast<float*>(smem), cb, tid);
 
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wk = wave & 1, wt = wave >> 1;

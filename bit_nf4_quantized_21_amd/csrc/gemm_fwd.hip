@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int tile = __builtin_amdgcn_readfirstlane(item / p.S), sidx = __builtin_amdgcn_readfirstlane(item % p.S);
   const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
 
-  if (tid < 16) lut[tid] = cb.c[tid];
+  codebook_to_lds(lut, cb, tid);
 
   const int wave = tid >> 6, lane = tid & 63, ml = lane & 31, h = lane >> 5;
   const int64_t T = p.T, K = p.K, N = p.N;

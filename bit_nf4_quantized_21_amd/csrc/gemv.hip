@@ -12,8 +12,8 @@
 // owns one row and 32 consecutive k of a chunk (16 code bytes, one 16-byte
 // load); the codes are decoded in registers straight into the A operand of a
 // bf16 16x16x32 MFMA whose B operand is X padded to 16 token columns.  Loads
-// are issued two chunks ahead of the decode so that a wave keeps ~8 KB of
-// HBM traffic in flight.
+// are issued four chunks ahead of the decode, the first four before the
+// workgroup's other set-up, so a wave keeps ~16 KB of traffic in flight.
 #include "common.hpp"
 #include "timing.hpp"
 #include "gemm.hpp"
@@ -34,7 +34,7 @@ struct ChunkRegs {
 };
 
 __global__ __launch_bounds__(512) void gemv_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  __shared__ float lut[16];
+  __shared__ __align__(16) float lut[16];
   __shared__ float red[kWaves][16][17];
   __shared__ float xa_s[16][kMaxR + 1];
   __shared__ float b_s[kMaxR][17];
@@ -45,54 +45,73 @@ __global__ __launch_bounds__(512) void gemv_fwd_kernel(FwdGemmParams p, Codebook
   const int r = p.r;
   const int64_t n0 = (int64_t)blockIdx.x * kRowsPerWG;
   const int64_t n = n0 + l16;
-  const bool nval = n < N;
-  const bool tval = l16 < T;
   const int64_t K2 = K / 2, bpr = K / 64;
 
-  if (tid < 16) lut[tid] = cb.c[tid];
-  for (int i = tid; i < (int)T * r; i += 512) xa_s[i / r][i % r] = p.XA[i];
-  for (int i = tid; i < r * kRowsPerWG; i += 512) {
-    const int j = i / kRowsPerWG, nn = i % kRowsPerWG;
-    b_s[j][nn] = (n0 + nn < N) ? bf16_to_f32(p.B[(int64_t)j * N + n0 + nn]) : 0.0f;
-  }
-  __syncthreads();
-
   const int64_t nchunk = (K + 127) / 128;
+  // Unconditional buffer loads (reads past a view's end return zero): rows
+  // n >= N read zero codes and scales; a 32-k group past K reads some other
+  // row's codes but a zero X (its offset is pushed out of range), so it adds
+  // nothing.  Chunks past the last are loaded and never used.
+  const rsrc_t rc = make_rsrc(p.codes, N * K2);
+  const rsrc_t rq = make_rsrc(p.q8, N * bpr);
+  const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
+  const rsrc_t rx = make_rsrc(p.X, T * K * 2);
   auto load = [&](int64_t c, ChunkRegs& R) {
     const int64_t k0 = c * 128 + 32 * g;
     const bool kv = k0 < K;  // K % 64 == 0: a 32-k group is whole or absent
-    if (nval && kv) {
-      R.c = *reinterpret_cast<const u32x4*>(p.codes + n * K2 + k0 / 2);
-      const int64_t b = n * bpr + k0 / 64;
-      R.q = p.q8[b];
-      R.s2 = p.s2[b >> 8];
-    } else {
-      R.c = u32x4{0u, 0u, 0u, 0u};
-      R.q = 0u;
-      R.s2 = 0.0f;
-    }
+    R.c = buf_load16(rc, (uint32_t)(n * K2 + k0 / 2));
+    const int64_t b = n * bpr + k0 / 64;
+    R.q = buf_load1(rq, (uint32_t)b);
+    R.s2 = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
+    const uint32_t xo = kv ? (uint32_t)(((int64_t)l16 * K + k0) * 2) : 0x7FFFFF00u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      R.x[s] = (tval && kv) ? *reinterpret_cast<const u32x4*>(p.X + (int64_t)l16 * K + k0 + 8 * s)
-                            : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) R.x[s] = buf_load16(rx, xo + 16 * s);
   };
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  ChunkRegs R0 = {}, R1 = {}, R2 = {};
-  int64_t c = wave;
-  if (c < nchunk) load(c, R0);
-  if (c + kWaves < nchunk) load(c + kWaves, R1);
-  for (; c < nchunk; c += kWaves) {
-    if (c + 2 * kWaves < nchunk) load(c + 2 * kWaves, R2);
-    const float sc = dq_scale(R0.q, R0.s2);
+  // The adapter operands (XA, T*r <= 2048 floats, and the workgroup's r x 16
+  // slice of B) are requested first from clamped, in-bounds addresses, then
+  // the first four weight chunks of every wave; the adapter values are stored
+  // to LDS once they arrive, which waits for nothing issued after them.
+  const int nx = (int)T * r, nbv = r * kRowsPerWG;
+  float xv[4];
+  uint16_t bv[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint32_t o[4];
-      decode8_bf16(R0.c[s], sc, lut, o);
-      acc = mfma16(as_bf16x8(o[0], o[1], o[2], o[3]), as_bf16x8(R0.x[s]), acc);
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 512 * k;
+    xv[k] = p.XA[i < nx ? i : nx - 1];
+    const int ib = i < nbv ? i : nbv - 1;
+    const int64_t nn = n0 + ib % kRowsPerWG;
+    bv[k] = p.B[(int64_t)(ib / kRowsPerWG) * N + (nn < N ? nn : N - 1)];
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  ChunkRegs R[4] = {};
+  const int64_t c0 = wave;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load(c0 + i * kWaves, R[i]);
+
+  codebook_to_lds(lut, cb, tid);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 512 * k;
+    if (i < nx) xa_s[i / r][i % r] = xv[k];
+    if (i < nbv) b_s[i / kRowsPerWG][i % kRowsPerWG] = n0 + i % kRowsPerWG < N ? bf16_to_f32(bv[k]) : 0.0f;
+  }
+  __syncthreads();
+
+  for (int64_t cb0 = c0; cb0 < nchunk; cb0 += 4 * kWaves) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t c = cb0 + i * kWaves;
+      if (c >= nchunk) break;
+      const float sc = dq_scale(R[i].q, R[i].s2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t o[4];
+        decode8_bf16(R[i].c[s], sc, lut, o);
+        acc = mfma16(as_bf16x8(o[0], o[1], o[2], o[3]), as_bf16x8(R[i].x[s]), acc);
+      }
+      load(c + 4 * kWaves, R[i]);
     }
-    R0 = R1;
-    R1 = R2;
   }
   // D[n][t]: lane holds column t = l16 and rows n = 4g + i.
 #pragma unroll

@@ -222,8 +222,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
                                                          const uint8_t* __restrict__ q8,
                                                          const float* __restrict__ s2, int64_t n,
                                                          int out_bf16, void* __restrict__ out, Codebook cb) {
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = cb.c[threadIdx.x];
+  __shared__ __align__(16) float lut[16];
+  codebook_to_lds(lut, cb, threadIdx.x);
   __syncthreads();
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e0 >= n) return;
