@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "splitk.hpp"
 
 namespace qlora {
 
@@ -21,10 +22,10 @@ struct FwdGemmParams {
   int64_t T, K, N;
   int r, RP;             // RP = r rounded up to 64
   float s;
-  float* slots;          // split partials: tiles * S * 65536 floats (S > 1)
-  int* counters;         // one per tile, zero on entry, left zero
-  int S;                 // contraction slices per tile (GEMM only)
-  int tiles_n, tiles_m, per_xcd, steps_per;  // filled by the launcher
+  float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
+  int* counters;         // one per split tile, zero on entry, left zero
+  SplitPlan plan;        // filled by the launcher
+  int tiles_n, tiles_m;  // filled by the launcher
 };
 
 struct DxGemmParams {
@@ -38,23 +39,19 @@ struct DxGemmParams {
   uint16_t* dX;          // [T,K] bf16
   int64_t T, K, N;
   int r, RP;            // RP = r rounded up to 64
-  float* slots;          // split partials: tiles * S * 65536 floats (S > 1)
-  int* counters;         // one per tile, zero on entry, left zero
-  int S;                 // contraction slices per tile
-  int tiles_k, tiles_t, per_xcd, steps_per;
+  float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
+  int* counters;         // one per split tile, zero on entry, left zero
+  SplitPlan plan;        // filled by the launcher
+  int tiles_k, tiles_t;
 };
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
 hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
 hipError_t launch_gemm_dx(const DxGemmParams& p, const Codebook& cb, hipStream_t s);
 
-// Tile grid of the dX GEMM: tiles and contraction slices for a T x K x N
-// problem (the workspace of the backward pass is sized from these).
-struct DxGrid {
-  int64_t tiles;
-  int S;
-};
-DxGrid dx_grid(int64_t T, int64_t K, int64_t N);
-DxGrid fwd_grid(int64_t T, int64_t K, int64_t N);
+// Work plans of the two GEMMs for a T x K x N problem (the workspaces are
+// sized from these).
+SplitPlan dx_plan(int64_t T, int64_t K, int64_t N);
+SplitPlan fwd_plan(int64_t T, int64_t K, int64_t N);
 
 }  // namespace qlora

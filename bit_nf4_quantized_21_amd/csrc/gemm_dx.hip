@@ -67,13 +67,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   __shared__ __align__(1024) unsigned char smem[kSmem];
   const int tid = threadIdx.x;
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; each XCD takes a
-  // contiguous run of (tile, slice) items, so the slices of a tile share an
-  // L2 for their partial sums.
-  const int bid = blockIdx.x;
-  const int item = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (item >= p.tiles_k * p.tiles_t * p.S) return;  // uniform per workgroup, before any barrier
-  const int tile = item / p.S, sidx = item % p.S;
+  // Workgroups are dispatched round-robin over the 8 XCDs; each XCD works
+  // through its own contiguous run of tiles (whole tiles first, then the
+  // contraction slices of the rest), so the slices of a tile share an L2.
+  const TileItem it = decode_item(p.plan, blockIdx.x);
+  if (it.tile < 0) return;  // uniform per workgroup, before any barrier
+  const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
   // Workgroup-uniform values kept in scalar registers (the buffer views
   // built from them must be uniform).
   const int tk = __builtin_amdgcn_readfirstlane(tile / p.tiles_t);
@@ -86,8 +85,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   const int64_t k0 = (int64_t)tk * kTileK, t0 = (int64_t)tt * kTileT;
   const int64_t K2 = K / 2, bpr = K / 64;
   const int nsteps = (int)((N + 63) / 64);
-  const int jbeg = sidx * p.steps_per;
-  const int jend = jbeg + p.steps_per < nsteps ? jbeg + p.steps_per : nsteps;
+  const int jbeg = __builtin_amdgcn_readfirstlane(it.kbeg), jend = __builtin_amdgcn_readfirstlane(it.kend);
+  (void)nsteps;
 
   // dY staging: lane -> rows xr + 32 i of the tile, 16-byte chunk xc.
   const int xc = tid & 7, xr = tid >> 3;
@@ -306,8 +305,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   }
 #undef QLORA_DX_MFMA
 
-  if (p.S > 1 && !splitk_combine(acc, p.slots + (int64_t)tile * p.S * kSplitSlotFloats, p.counters + tile, p.S,
-                                 sidx, reinterpret_cast<int*>(smem + kS0)))
+  if (it.S > 1 && !splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats,
+                                  p.counters + it.ordinal, it.S, sidx, reinterpret_cast<int*>(smem + kS0)))
     return;
 
   // D[k][t]: lane holds column t and rows k = 8*q4 + 4h + (0..3) of each 32x32 tile.
@@ -330,24 +329,18 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   }
 }
 
-DxGrid dx_grid(int64_t T, int64_t K, int64_t N) {
-  DxGrid g;
-  g.tiles = ((K + kTileK - 1) / kTileK) * ((T + kTileT - 1) / kTileT);
-  g.S = choose_split(g.tiles, (N + 63) / 64);
-  return g;
+SplitPlan dx_plan(int64_t T, int64_t K, int64_t N) {
+  return make_split_plan(((K + kTileK - 1) / kTileK) * ((T + kTileT - 1) / kTileT), (N + 63) / 64);
 }
 
 hipError_t launch_gemm_dx(const DxGemmParams& p0, const Codebook& cb, hipStream_t s) {
   DxGemmParams p = p0;
   p.tiles_k = (int)((p.K + kTileK - 1) / kTileK);
   p.tiles_t = (int)((p.T + kTileT - 1) / kTileT);
-  const int64_t nsteps = (p.N + 63) / 64;
-  p.steps_per = (int)((nsteps + p.S - 1) / p.S);
-  const int total = p.tiles_k * p.tiles_t * p.S;
-  p.per_xcd = (total + 7) / 8;
+  p.plan = dx_plan(p.T, p.K, p.N);
   {
     KernelTimer kt_("gemm_dx_kernel", s);
-    hipLaunchKernelGGL(gemm_dx_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+    hipLaunchKernelGGL(gemm_dx_kernel, dim3(8 * p.plan.items), dim3(256), 0, s, p, cb);
   }
   return hipGetLastError();
 }

@@ -65,10 +65,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // token-tile-major and each XCD takes a contiguous run of them, so the X
   // tile (the operand re-read by every n-tile) stays in that XCD's L2.
   // Items are (tile, contraction slice) pairs, slices of a tile adjacent.
-  const int bid = blockIdx.x;
-  const int item = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (item >= p.tiles_n * p.tiles_m * p.S) return;  // uniform per workgroup, before any barrier
-  const int tile = __builtin_amdgcn_readfirstlane(item / p.S), sidx = __builtin_amdgcn_readfirstlane(item % p.S);
+  const TileItem it = decode_item(p.plan, blockIdx.x);
+  if (it.tile < 0) return;  // uniform per workgroup, before any barrier
+  const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
   const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
 
   codebook_to_lds(lut, cb, tid);
@@ -78,8 +77,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int64_t n0 = (int64_t)tn * kTileN, m0 = (int64_t)tm * kTileM;
   const int64_t K2 = K / 2, bpr = K / 64;
   const int nk = (int)(K / 64);
-  const int kbeg = sidx * p.steps_per;
-  const int kend = kbeg + p.steps_per < nk ? kbeg + p.steps_per : nk;
+  const int kbeg = __builtin_amdgcn_readfirstlane(it.kbeg), kend = __builtin_amdgcn_readfirstlane(it.kend);
   auto clampk = [&](int k) { return k < nk ? k : nk - 1; };  // past the end: redundant, in bounds
 
   // Buffer views of this tile's rows: reads past the last row return zero.
@@ -339,10 +337,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     }
   }
 
-  if (p.S > 1) {
+  if (it.S > 1) {
     __syncthreads();  // every wave is done with LDS; word 16 holds the ticket
-    if (!splitk_combine(acc, p.slots + (int64_t)tile * p.S * kSplitSlotFloats, p.counters + tile, p.S, sidx,
-                        reinterpret_cast<int*>(smem + 64)))
+    if (!splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats, p.counters + it.ordinal,
+                        it.S, sidx, reinterpret_cast<int*>(smem + 64)))
       return;
   }
 
@@ -366,24 +364,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   }
 }
 
-DxGrid fwd_grid(int64_t T, int64_t K, int64_t N) {
-  DxGrid g;
-  g.tiles = ((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
-  g.S = choose_split(g.tiles, K / 64);
-  return g;
+SplitPlan fwd_plan(int64_t T, int64_t K, int64_t N) {
+  return make_split_plan(((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM), K / 64);
 }
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p0, const Codebook& cb, hipStream_t s) {
   FwdGemmParams p = p0;
   p.tiles_n = (int)((p.N + kTileN - 1) / kTileN);
   p.tiles_m = (int)((p.T + kTileM - 1) / kTileM);
-  const int64_t nk = p.K / 64;
-  p.steps_per = (int)((nk + p.S - 1) / p.S);
-  const int total = p.tiles_n * p.tiles_m * p.S;
-  p.per_xcd = (total + 7) / 8;
+  p.plan = fwd_plan(p.T, p.K, p.N);
   {
     KernelTimer kt_("gemm_fwd_kernel", s);
-    hipLaunchKernelGGL(gemm_fwd_kernel, dim3(8 * p.per_xcd), dim3(256), 0, s, p, cb);
+    hipLaunchKernelGGL(gemm_fwd_kernel, dim3(8 * p.plan.items), dim3(256), 0, s, p, cb);
   }
   return hipGetLastError();
 }

@@ -65,9 +65,9 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * RP * N * sizeof(float);
   const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * RP * K * sizeof(float);
   l.ptok = align256(pdb > pda ? pdb : pda);
-  const DxGrid dg = dx_grid(T, K, N);
-  l.slots = dg.S > 1 ? align256((size_t)dg.tiles * dg.S * kSplitSlotFloats * sizeof(float)) : 0;
-  l.counters = align256((size_t)dg.tiles * sizeof(int));
+  const SplitPlan dp = dx_plan(T, K, N);
+  l.slots = dp.S > 1 ? align256((size_t)dp.nsplit() * dp.S * kSplitSlotFloats * sizeof(float)) : 0;
+  l.counters = align256((size_t)(dp.nsplit() > 0 ? dp.nsplit() : 1) * sizeof(int));
   l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok + l.slots + l.counters;
   return l;
 }
@@ -77,16 +77,16 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
 // tile counters.
 struct FwdLayout {
   size_t p, xah, slots, counters, total;
-  DxGrid g;
+  SplitPlan g;
 };
 FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   FwdLayout l{};
   l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
   if (T > kGemvMaxT) {
     l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
-    l.g = fwd_grid(T, K, N);
-    l.slots = l.g.S > 1 ? align256((size_t)l.g.tiles * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
-    l.counters = align256((size_t)l.g.tiles * sizeof(int));
+    l.g = fwd_plan(T, K, N);
+    l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
+    l.counters = align256((size_t)(l.g.nsplit() > 0 ? l.g.nsplit() : 1) * sizeof(int));
   }
   l.total = l.p + 2 * l.xah + l.slots + l.counters;
   return l;
@@ -118,7 +118,7 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
     o.row_lo = XAl;
     o.scale_row = a.s;
     o.zero = reinterpret_cast<int*>(w2 + l.slots);  // the GEMM's split tickets
-    o.nzero = l.g.tiles;
+    o.nzero = l.g.nsplit();
   }
   hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
   if (e != hipSuccess) return e;
@@ -140,7 +140,6 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   p.RP = (int)rpad(a.r);
   p.slots = reinterpret_cast<float*>(w2);
   p.counters = reinterpret_cast<int*>(w2 + l.slots);
-  p.S = a.T > kGemvMaxT ? l.g.S : 1;
   return a.T <= kGemvMaxT ? launch_gemv_fwd(p, cb, s) : launch_gemm_fwd(p, cb, s);
 }
 
@@ -164,7 +163,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   float* Ptok = reinterpret_cast<float*>(w2 + 4 * l.planes);
   float* slots = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok);
   int* counters = reinterpret_cast<int*>(w2 + 4 * l.planes + l.ptok + l.slots);
-  const DxGrid dg = dx_grid(a.T, a.K, a.N);
+  const SplitPlan dp = dx_plan(a.T, a.K, a.N);
   const int64_t TP = round_up(a.T, 64);
 
   // G = dY B^T as the bf16 hi / lo rows of s G (the dX GEMM's adapter step)
@@ -180,7 +179,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   o.side_hi = XAth;
   o.side_lo = XAtl;
   o.zero = counters;  // the dX GEMM's split tickets
-  o.nzero = dg.tiles;
+  o.nzero = dp.nsplit();
   hipError_t e = launch_rowdot(dY, a.B, /*v_lr=*/false, Pg, o, a.T, a.N, a.r, row_chunk(a.T, a.N), s);
   if (e != hipSuccess) return e;
   e = launch_tokdot(dY, XAth, XAtl, TP, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*m_major=*/false, s);
@@ -201,7 +200,6 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   p.RP = (int)rpad(a.r);
   p.slots = slots;
   p.counters = counters;
-  p.S = dg.S;
   e = launch_gemm_dx(p, cb, s);
   if (e != hipSuccess) return e;
   return launch_tokdot(X, Gth, Gtl, TP, Ptok, dA, a.T, a.K, a.r, tok_chunk(a.T, a.K), a.s, /*m_major=*/true, s);

@@ -61,19 +61,75 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
   return true;
 }
 
-// Number of slices for a grid of `tiles` tiles of `steps` contraction steps
-// on 256 compute units: split only to fill otherwise idle units (measured on
-// the 7B MLP shapes, splitting a grid that already covers the chip costs more
-// in partial-sum traffic and per-workgroup start-up than the shorter last
-// round saves).
-inline int choose_split(int64_t tiles, int64_t steps) {
-  int best = 1;
-  for (int S = 2; S <= 4; ++S) {
-    if (tiles * S > 256 || S > steps) break;
-    if ((steps + S - 1) / S * (S - 1) >= steps) continue;  // no empty slice
-    best = S;
+// Work plan of a tile grid on the 8 XCDs x 32 compute units.  Workgroup b
+// runs on XCD b % 8; XCD x owns the contiguous tiles [x*tx, x*tx + tx).  Its
+// first `full` tiles run whole; when the rest would fill at most half of the
+// XCD's units in a last round, each of them is cut into S contraction slices
+// so that the last round finishes sooner.  Items of an XCD are numbered in
+// dispatch order (whole tiles first), slices of a tile adjacent.
+struct SplitPlan {
+  int tiles;      // real tiles
+  int tx;         // tiles per XCD
+  int full;       // whole tiles per XCD
+  int S;          // slices of each remaining tile (1: none)
+  int items;      // items per XCD
+  int steps;      // contraction steps of a tile
+  int steps_per;  // contraction steps of a slice
+  int nsplit() const { return 8 * (tx - full); }  // split tiles, including any past `tiles`
+};
+
+inline SplitPlan make_split_plan(int64_t tiles, int64_t steps) {
+  SplitPlan pl{};
+  pl.tiles = (int)tiles;
+  pl.steps = (int)steps;
+  pl.tx = (int)((tiles + 7) / 8);
+  const int rem = pl.tx <= 32 ? pl.tx : pl.tx % 32;
+  pl.full = pl.tx - rem;
+  pl.S = 1;
+  if (rem > 0 && rem <= 16) {
+    for (int S = 2; S <= 4; ++S) {
+      if (rem * S > 32 || S > steps) break;
+      if ((steps + S - 1) / S * (S - 1) >= steps) continue;  // no empty slice
+      pl.S = S;
+    }
   }
-  return best;
+  if (pl.S == 1) pl.full = pl.tx;
+  pl.items = pl.full + (pl.tx - pl.full) * pl.S;
+  pl.steps_per = (int)((steps + pl.S - 1) / pl.S);
+  return pl;
+}
+
+struct TileItem {
+  int tile;     // tile index, or -1: nothing to do
+  int sidx;     // slice
+  int S;        // slices of this tile
+  int ordinal;  // index among split tiles (slots / counter), -1 when whole
+  int kbeg, kend;
+};
+
+__device__ __forceinline__ TileItem decode_item(const SplitPlan& pl, int bid) {
+  TileItem it;
+  const int xcd = bid & 7, local = bid >> 3;
+  it.tile = -1;
+  if (local >= pl.items) return it;
+  if (local < pl.full) {
+    it.tile = xcd * pl.tx + local;
+    it.sidx = 0;
+    it.S = 1;
+    it.ordinal = -1;
+    it.kbeg = 0;
+    it.kend = pl.steps;
+  } else {
+    const int idx = local - pl.full;
+    it.tile = xcd * pl.tx + pl.full + idx / pl.S;
+    it.sidx = idx % pl.S;
+    it.S = pl.S;
+    it.ordinal = xcd * (pl.tx - pl.full) + idx / pl.S;
+    it.kbeg = it.sidx * pl.steps_per;
+    it.kend = it.kbeg + pl.steps_per < pl.steps ? it.kbeg + pl.steps_per : pl.steps;
+  }
+  if (it.tile >= pl.tiles) it.tile = -1;
+  return it;
 }
 
 }  // namespace qlora
