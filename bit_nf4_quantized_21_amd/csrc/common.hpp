@@ -141,6 +141,16 @@ __device__ __forceinline__ uint32_t bfe(uint32_t x) {
   return r;
 }
 
+// Byte q (0..3, a constant once unrolled) of x, by one v_bfe_u32.
+__device__ __forceinline__ uint32_t bfe8(uint32_t x, int q) {
+  switch (q) {
+    case 0: return bfe<0, 8>(x);
+    case 1: return bfe<8, 8>(x);
+    case 2: return bfe<16, 8>(x);
+    default: return bfe<24, 8>(x);
+  }
+}
+
 // Codebook values of the 8 codes of a dword, element e = nibble e, from the
 // 16-entry fp32 table at LDS address 0 (`lds` points there): byte q of
 // (x << 2) & 0x3C3C3C3C is 4 * code(2q), of (x >> 2) & 0x3C3C3C3C is

@@ -110,6 +110,22 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x4*>(xring[stage] + ((j & 1) ? xl_odd : xl_even) + 8 * j * 128) = xr[j];
   };
+  auto load_x_row = [&](int kb, int j) -> u32x4 { return buf_load16(rx, xg + (uint32_t)(8 * j * K * 2 + kb * 128)); };
+  auto store_x_row = [&](int stage, int j, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(xring[stage] + ((j & 1) ? xl_odd : xl_even) + 8 * j * 128) = v;
+  };
+  // One of the six loads of load_w: part 3g + {0: codes, 1: q8, 2: s2}.
+  auto load_w_part = [&](int kb, u32x4(&c)[2], uint32_t(&q)[2], float(&sv)[2], int part) {
+    const int g = part / 3;
+    if (part % 3 == 0) {
+      c[g] = buf_load16(rc, (uint32_t)(nl[g] * K2 + kb * 32 + 16 * h));
+    } else if (part % 3 == 1) {
+      q[g] = buf_load1(rq, (uint32_t)(nl[g] * bpr + kb));
+    } else {
+      const int64_t b = (n0 + nl[g]) * bpr + kb;
+      sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
+    }
+  };
   auto load_w = [&](int kb, u32x4(&c)[2], uint32_t(&q)[2], float(&sv)[2]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -173,82 +189,74 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   load_w(clampk(kbeg + 1), cA, qA, sA);
   read_x(0, 0, xa);
 
-  // Substep S: MFMAs on (wc[.][S], XCUR); X of the next substep -> XNXT;
-  // PACK the chunk pending in fp; fetch the codebook values of chunk S of
-  // the next step (codes CA) into fp.
-#define QLORA_FWD_SUBSTEP(S, XCUR, XNXT, NXTSTAGE, NXTS, CA, PACK)                      \
-  {                                                                                     \
-    read_x(NXTSTAGE, NXTS, XNXT);                                                       \
-    PACK;                                                                               \
-    lut8(CA[0][S], fp[0]);                                                              \
-    lut8(CA[1][S], fp[1]);                                                              \
-    _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
-      acc[0][mi] = mfma32(wc[0][S], XCUR[mi], acc[0][mi]);                              \
-      acc[1][mi] = mfma32(wc[1][S], XCUR[mi], acc[1][mi]);                              \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                    \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
-    }                                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                  \
-  }
-  // Substep 3 also writes X(kb+2) from registers to its stage and reloads the
-  // registers with X(kb+3); the writes and loads are spread over the MFMAs.
-#define QLORA_FWD_SUBSTEP3(XCUR, XNXT, NXTSTAGE, WSTAGE, KN3, CA, PACK)                   \
-  {                                                                                     \
-    store_x(WSTAGE, xr);                                                                \
-    load_x(KN3, xr);                                                                    \
-    read_x(NXTSTAGE, 0, XNXT);                                                          \
-    PACK;                                                                               \
-    lut8(CA[0][3], fp[0]);                                                              \
-    lut8(CA[1][3], fp[1]);                                                              \
-    _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
-      acc[0][mi] = mfma32(wc[0][3], XCUR[mi], acc[0][mi]);                              \
-      acc[1][mi] = mfma32(wc[1][3], XCUR[mi], acc[1][mi]);                              \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                \
-    }                                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                  \
+  // Substep S of a step: 16 slices, each one MFMA on (wc[.][S], XCUR) plus
+  // at most one piece of each kind of side work, fenced off from the next
+  // slice so the issue order stays interleaved:
+  //  * slices 0..7 read X of the next substep (XNXT, ring stage RSTAGE,
+  //    chunk RS) and scale + pack one bf16 pair of the chunk pending in fp
+  //    (scales SCL) into WARR[.][WIDX];
+  //  * every slice looks up one codebook value of chunk S of the next step's
+  //    codes CA into fp (element i of slice i; a pair is packed in slice
+  //    i/2 or earlier, so the old value is consumed before it is replaced);
+  //  * EXTRA(i) adds the step's memory traffic and scale arithmetic.
+#define QLORA_FWD_SUBSTEP(S, XCUR, XNXT, RSTAGE, RS, CA, WARR, WIDX, SCL, EXTRA)                   \
+  {                                                                                               \
+    const unsigned char* xs_ = xring[RSTAGE] + ml * 128 + (((4 * h + (RS)) ^ sw) << 4);           \
+    uint32_t y4_[2], z4_[2], pw_[2][4];                                                           \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                              \
+      acc[i & 1][i >> 1] = mfma32(wc[i & 1][S], XCUR[i >> 1], acc[i & 1][i >> 1]);                \
+      if (i < 8) {                                                                                \
+        XNXT[i] = *reinterpret_cast<const bf16x8*>(xs_ + i * 4096);                              \
+        const int g_ = i >> 2, q_ = i & 3;                                                        \
+        pw_[g_][q_] = pack_bf16x2(fp[g_][2 * q_] * SCL[g_], fp[g_][2 * q_ + 1] * SCL[g_]);        \
+        if (q_ == 3) WARR[g_][WIDX] = as_bf16x8(pw_[g_][0], pw_[g_][1], pw_[g_][2], pw_[g_][3]); \
+      }                                                                                           \
+      if ((i & 7) == 0) {                                                                         \
+        y4_[i >> 3] = (CA[i >> 3][S] << 2) & 0x3C3C3C3Cu;                                        \
+        z4_[i >> 3] = (CA[i >> 3][S] >> 2) & 0x3C3C3C3Cu;                                        \
+      }                                                                                           \
+      fp[i >> 3][i & 7] = *reinterpret_cast<const float*>(                                        \
+          smem + bfe8(((i & 1) ? z4_ : y4_)[i >> 3], (i & 7) >> 1));                              \
+      EXTRA;                                                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                          \
+    }                                                                                             \
   }
 
   // One pipelined step on ring stage ST (the next two steps' stages are ST1,
-  // ST2).  CA..
-  // name the register set holding the codes of step kb+1 (decoded now), CB..
-  // the set that receives the codes of step kb+2.  The loop is unrolled by
-  // six so code sets (period 2) and stages (period 3) are compile-time
-  // constants: no register copies (a copy would wait for the load just
-  // issued) and statically distinct LDS objects.
+  // ST2).  CA.. name the register set holding the codes of step kb+1
+  // (decoded now), CB.. the set that receives the codes of step kb+2.  The
+  // loop is unrolled by six so code sets (period 2) and stages (period 3)
+  // are compile-time constants: no register copies (a copy would wait for
+  // the load just issued) and statically distinct LDS objects.
+  //  * substep 0 loads the codes of step kb+2 (slices 8..13) and computes
+  //    the scales of CA (slices 14, 15);
+  //  * substep 3 moves X(kb+2) from registers to stage ST2 and reloads the
+  //    registers with X(kb+3) (slices 8..15).
+  // Every wave wrote its rows of X(kb+1) into ST1 one step ago; the barrier
+  // before substep 3 makes them visible before substep 3 reads them, and
+  // every wave is done with stage ST2 (last read in step kb-1) by then.  At
+  // most 8 of this wave's LDS operations are left in flight across it: the
+  // stage writes are older than the last 8.
 #define QLORA_FWD_STEP(KB, ST, ST1, ST2, CA, QA, SA, CB, QB, SB)                                       \
   {                                                                                                    \
-    const int st = (ST), st1 = (ST1), st2 = (ST2);                                                     \
     const int kn2 = (KB) + 2 < nk ? (KB) + 2 : nk - 1; /* past the end: redundant, in bounds */        \
     const int kn3 = (KB) + 3 < nk ? (KB) + 3 : nk - 1;                                                 \
-    load_w(kn2, CB, QB, SB);                                                                           \
-    const float sc0 = dq_scale(QA[0], SA[0]), sc1 = dq_scale(QA[1], SA[1]);                             \
-    __builtin_amdgcn_sched_barrier(0);                                                                 \
-    QLORA_FWD_SUBSTEP(0, xa, xb, st, 1, CA,                                                            \
-                      { wc[0][3] = pack8(fp[0], scp[0]); wc[1][3] = pack8(fp[1], scp[1]); })            \
-    QLORA_FWD_SUBSTEP(1, xb, xa, st, 2, CA, { wn[0][0] = pack8(fp[0], sc0); wn[1][0] = pack8(fp[1], sc1); }) \
-    QLORA_FWD_SUBSTEP(2, xa, xb, st, 3, CA, { wn[0][1] = pack8(fp[0], sc0); wn[1][1] = pack8(fp[1], sc1); }) \
-    /* Every wave wrote its rows of X(kb+1) one step ago; after the barrier  */                       \
-    /* they are visible, and every wave is done with stage st2 (last read  */                         \
-    /* in step kb-1), which receives X(kb+2).                                */                       \
-    lds_barrier();                                                                                     \
-    QLORA_FWD_SUBSTEP3(xb, xa, st1, st2, kn3, CA,                                                      \
-                       { wn[0][2] = pack8(fp[0], sc0); wn[1][2] = pack8(fp[1], sc1); })                 \
-    scp[0] = sc0;                                                                                      \
-    scp[1] = sc1;                                                                                      \
+    float sc[2];                                                                                       \
+    QLORA_FWD_SUBSTEP(0, xa, xb, ST, 1, CA, wc, 3, scp, {                                              \
+      if (i >= 8 && i < 14) load_w_part(kn2, CB, QB, SB, i - 8);                                       \
+      if (i >= 14) sc[i - 14] = dq_scale(QA[i - 14], SA[i - 14]);                                      \
+    })                                                                                                 \
+    QLORA_FWD_SUBSTEP(1, xb, xa, ST, 2, CA, wn, 0, sc, {})                                             \
+    QLORA_FWD_SUBSTEP(2, xa, xb, ST, 3, CA, wn, 1, sc, {})                                             \
+    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");                                    \
+    QLORA_FWD_SUBSTEP(3, xb, xa, ST1, 0, CA, wn, 2, sc, {                                              \
+      if (i >= 8) {                                                                                    \
+        store_x_row(ST2, i - 8, xr[i - 8]);                                                            \
+        xr[i - 8] = load_x_row(kn3, i - 8);                                                            \
+      }                                                                                                \
+    })                                                                                                 \
+    scp[0] = sc[0];                                                                                    \
+    scp[1] = sc[1];                                                                                    \
     _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                                    \
       _Pragma("unroll") for (int s = 0; s < 3; ++s) wc[g][s] = wn[g][s];                              \
     }                                                                                                  \
@@ -275,7 +283,6 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   }
 #undef QLORA_FWD_STEP
 #undef QLORA_FWD_SUBSTEP
-#undef QLORA_FWD_SUBSTEP3
 
   // LoRA up-projection as two more K-steps of 64 j per pass: A operand =
   // B^T (rows n), B operand = the bf16 hi and lo rows of s XA (rows m), so
