@@ -45,6 +45,7 @@ constexpr int kLut = 1024;       // codebook slot at address 0
 constexpr int kW0 = kLut, kW1 = kW0 + kBuf, kD0 = kW1 + kBuf, kD1 = kD0 + kBuf, kS0 = kD1 + kBuf;
 constexpr int kSBytes = 4 * 64 * 4;  // [4 k-blocks][64 rows] fp32 scales
 constexpr int kSmem = kS0 + 2 * kSBytes;
+static_assert(kS0 >= 256 * 512, "the dX staging tile fits below the scale tables");
 
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ (((row >> 1) ^ (row >> 4)) & 7)) << 4));
@@ -309,23 +310,32 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
                                   p.counters + it.ordinal, it.S, sidx, reinterpret_cast<int*>(smem + kS0)))
     return;
 
-  // D[k][t]: lane holds column t and rows k = 8*q4 + 4h + (0..3) of each 32x32 tile.
+  // dX through LDS: D[k][t] of a 32x32 tile gives lane (l32, h) token
+  // t = 128 wt + 32 b + l32 and the 4 features 8 q4 + 4h + (0..3) of k-block
+  // 128 wk + 32 a, written as bf16 into a [256 t][256 k] tile whose 16-byte
+  // chunks are XOR-swizzled by the row (the 32 lanes of a write land in 32
+  // distinct chunks); then each 32 lanes store one whole 512-byte row of dX.
+  __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int64_t t = t0 + 128 * wt + 32 * b + l32;
-    if (t >= T) continue;
+    const int row = 128 * wt + 32 * b + l32;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int64_t k = k0 + 128 * wk + 32 * a + 8 * q4 + 4 * h;
-        if (k < K) {
-          const f32x16& v = acc[a][b];
-          uint2 o = make_uint2(pack_bf16x2(v[4 * q4 + 0], v[4 * q4 + 1]), pack_bf16x2(v[4 * q4 + 2], v[4 * q4 + 3]));
-          *reinterpret_cast<uint2*>(p.dX + t * K + k) = o;
-        }
+        const int c = 16 * wk + 4 * a + q4;
+        const f32x16& v = acc[a][b];
+        *reinterpret_cast<uint2*>(smem + row * 512 + ((c ^ l32) << 4) + 8 * h) =
+            make_uint2(pack_bf16x2(v[4 * q4 + 0], v[4 * q4 + 1]), pack_bf16x2(v[4 * q4 + 2], v[4 * q4 + 3]));
       }
-    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;
+    const int64_t t = t0 + row, k = k0 + 8 * c;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * 512 + ((c ^ (row & 31)) << 4));
+    if (t < T && k < K) *reinterpret_cast<u32x4*>(p.dX + t * K + k) = v;  // K % 64 == 0: chunks whole
   }
 }
 

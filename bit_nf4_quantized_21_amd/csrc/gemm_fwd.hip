@@ -51,6 +51,7 @@ constexpr int kTileN = 256;
 constexpr int kTileM = 256;
 constexpr int kStageBytes = kTileM * 128;  // one X stage: 256 rows x 64 bf16
 constexpr int kLutBytes = 1024;            // codebook slot (keeps stages 1 KiB aligned)
+static_assert(kLutBytes + 3 * kStageBytes >= 128 * 512, "the Y staging tile fits in LDS");
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codebook cb) {
@@ -351,22 +352,34 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       return;
   }
 
-  // D[n][m]: lane holds column m and rows n = 8*q4 + 4h + (0..3) of each 32x32 tile.
+  // Y through LDS, 128 token rows at a time: D[n][m] of a 32x32 tile gives
+  // lane (ml, h) token m = 32 mi + ml and the 4 features 8 q4 + 4h + (0..3),
+  // written as bf16 into a [128 m][256 n] tile whose 16-byte chunks are
+  // XOR-swizzled by the row (the 32 lanes of a write land in 32 distinct
+  // chunks); then each 32 lanes store one whole 512-byte row of Y.
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) {
-    const int64_t m = m0 + 32 * mi + ml;
-    if (m >= T) continue;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the stages (or the previous half) are free
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int mq = 0; mq < 4; ++mq) {
+      const int mi = 4 * half + mq, row = 32 * mq + ml;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int64_t n = n0 + 64 * wave + 32 * g + 8 * q4 + 4 * h;
-        if (n < N) {
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = 8 * wave + 4 * g + q4;
           const f32x16& a = acc[g][mi];
-          uint2 o = make_uint2(pack_bf16x2(a[4 * q4 + 0], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3]));
-          *reinterpret_cast<uint2*>(p.Y + m * N + n) = o;
+          *reinterpret_cast<uint2*>(smem + row * 512 + ((c ^ ml) << 4) + 8 * h) =
+              make_uint2(pack_bf16x2(a[4 * q4 + 0], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3]));
         }
-      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;
+      const int64_t m = m0 + 128 * half + row, n = n0 + 8 * c;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * 512 + ((c ^ (row & 31)) << 4));
+      if (m < T && n < N) *reinterpret_cast<u32x4*>(p.Y + m * N + n) = v;  // N % 8 == 0: chunks whole
     }
   }
 }
