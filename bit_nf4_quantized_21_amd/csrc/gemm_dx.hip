@@ -13,8 +13,8 @@
 //    The MFMA needs 8 consecutive n per lane, but the codes run along k, so
 //    W' goes through LDS transposed ([k][n]): each thread decodes an 8 x 8
 //    patch (8 rows n, 8 k = one code dword per row) and writes 8 16-byte
-//    columns, half of them (4 k for all 8 rows) every two substeps.  The codebook is read from LDS address 0 (one bitfield extract
-//    per lookup address).  The 8 per-row scales of a patch come from a table
+//    columns (4 k for all 8 rows at a time).  The codebook is read from LDS
+//    address 0 (one bitfield extract per lookup address).  The 8 per-row scales of a patch come from a table
 //    that the workgroup fills one step earlier, one fp64-exact scale per
 //    thread.
 //  * dY tiles are staged in LDS in their natural [t][n] layout from
@@ -24,8 +24,13 @@
 //    conflict-free and the transposed writes (rows 8 apart, all of one
 //    parity) are 2-way, the least their parity allows.
 //  * Software pipeline: while the MFMAs of step j run on buffers j % 2, the
-//    patch of step j+1 is decoded (two rows per substep) and written with
-//    dY(j+1) into buffers (j+1) % 2; one barrier per step.
+//    patch of step j+1 is decoded (its first lookups already in the last
+//    slices of step j-1) and written with dY(j+1) into buffers (j+1) % 2;
+//    one barrier per step, three quarters into it, after which the next
+//    step's first operands are read.  A step is 64 slices, each one MFMA
+//    plus a fixed share of the operand reads, lookups, packs, LDS writes and
+//    global loads, fenced from the next slice so the issue order stays
+//    interleaved; q8 / s2 are fetched a step before their scale is stored.
 //  * The adapter term is two more steps: A (rows k) against the bf16 hi and
 //    lo planes of s G (rows t), staged into the same buffers.
 //  * Workgroup order is XCD-aware (each XCD takes a contiguous run of
@@ -34,6 +39,9 @@
 #include "timing.hpp"
 #include "gemm.hpp"
 #include "splitk.hpp"
+
+#include <type_traits>
+#include <utility>
 
 namespace qlora {
 
@@ -47,21 +55,17 @@ constexpr int kSBytes = 4 * 64 * 4;  // [4 k-blocks][64 rows] fp32 scales
 constexpr int kSmem = kS0 + 2 * kSBytes;
 static_assert(kS0 >= 256 * 512, "the dX staging tile fits below the scale tables");
 
+// Calls f(integral_constant<int, I0 + i>) for i = 0, 1, ...: one straight-line
+// copy of the slice body per slice, with the slice index a constant.
+template <int I0, class F, int... Is>
+__device__ __forceinline__ void run_slices(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, I0 + Is>{}), ...);
+}
+
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ (((row >> 1) ^ (row >> 4)) & 7)) << 4));
 }
 
-// Codebook values (table at LDS address 0) of nibbles 4 HF .. 4 HF + 3 of a
-// code dword: byte q of (x << 2) & 0x3C3C3C3C is 4 * code(2q), of
-// (x >> 2) & 0x3C3C3C3C is 4 * code(2q + 1).
-template <int HF>
-__device__ __forceinline__ void lut4(const unsigned char* smem, uint32_t x, float (&f)[4]) {
-  const uint32_t y4 = (x << 2) & 0x3C3C3C3Cu, z4 = (x >> 2) & 0x3C3C3C3Cu;
-  f[0] = *reinterpret_cast<const float*>(smem + bfe<16 * HF, 8>(y4));
-  f[1] = *reinterpret_cast<const float*>(smem + bfe<16 * HF, 8>(z4));
-  f[2] = *reinterpret_cast<const float*>(smem + bfe<16 * HF + 8, 8>(y4));
-  f[3] = *reinterpret_cast<const float*>(smem + bfe<16 * HF + 8, 8>(z4));
-}
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codebook cb) {
@@ -103,67 +107,43 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // read zero and their scales are zero, so those W' rows vanish; k past K
   // has zero scales too.  dY rows are viewed from this tile's first row.
   const rsrc_t rc = make_rsrc(p.codes, N * K2);
+  const rsrc_t rq = make_rsrc(p.q8, N * bpr);
+  const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
   const rsrc_t rd = make_rsrc(p.dY + t0 * N, (T - t0) * N * 2);
   const uint32_t coff = (uint32_t)((8 * rg) * K2 + kcol / 2);
-  auto load_codes = [&](int j, uint32_t(&c)[8]) {
-    const uint32_t base = coff + (uint32_t)(j * 64 * K2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = buf_load4(rc, base + (uint32_t)(i * K2));
+  auto load_code = [&](int j, int i) -> uint32_t { return buf_load4(rc, coff + (uint32_t)(j * 64 * K2 + i * K2)); };
+  // q8 of this thread's scale entry (zero for a k-block past K) and its s2.
+  auto load_q = [&](int j) -> uint32_t {
+    const uint32_t q = buf_load1(rq, (uint32_t)(((int64_t)j * 64 + sr) * bpr + skb));
+    return sval ? q : 0u;
   };
-  auto load_qs = [&](int j, uint32_t& q, float& s2) {
-    const int64_t n = (int64_t)j * 64 + sr;
-    const bool ok = n < N && sval;
-    const int64_t b = n * bpr + skb;
-    q = ok ? (uint32_t)p.q8[b] : 0u;
-    s2 = ok ? p.s2[b >> 8] : 0.0f;
-  };
-  auto store_scale = [&](int sbuf, uint32_t q, float s2) {
-    reinterpret_cast<float*>(smem + kS0 + sbuf * kSBytes)[sb * 64 + sr] = dq_scale(q, s2);
+  auto load_s = [&](int j) -> float {
+    const int64_t b = ((int64_t)j * 64 + sr) * bpr + skb;
+    return __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
   };
   // Columns n >= N of the last step read the next row (or zero past the
   // end): finite values that meet zero W' rows.
   const uint32_t doff = (uint32_t)(xr * N * 2 + 16 * xc);
-  auto load_dy = [&](int j, u32x4(&v)[8]) {
-    const uint32_t base = doff + (uint32_t)(j * 128);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = buf_load16(rd, base + (uint32_t)(i * 32 * N * 2));
+  auto load_dy = [&](int j, int i) -> u32x4 { return buf_load16(rd, doff + (uint32_t)(j * 128 + i * 32 * N * 2)); };
+  auto store_row = [&](int base, int i, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(smem + base + swz(xr + 32 * i, xc)) = v;
   };
-  auto store_rows = [&](int base, const u32x4(&v)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(smem + base + swz(xr + 32 * i, xc)) = v[i];
+  auto scale_slot = [&](int sbuf) { return reinterpret_cast<float*>(smem + kS0 + sbuf * kSBytes) + sb * 64 + sr; };
+  auto read_scales = [&](int sbuf, int half, float(&sc)[8]) {
+    const float* t = reinterpret_cast<const float*>(smem + kS0 + sbuf * kSBytes) + (kq >> 3) * 64 + 8 * rg;
+    const float4 v = *reinterpret_cast<const float4*>(t + 4 * half);
+    sc[4 * half] = v.x; sc[4 * half + 1] = v.y; sc[4 * half + 2] = v.z; sc[4 * half + 3] = v.w;
   };
-  auto read_scales = [&](int sbuf, float(&sc)[8]) {
-    const float* s = reinterpret_cast<const float*>(smem + kS0 + sbuf * kSBytes) + (kq >> 3) * 64 + 8 * rg;
-    const float4 a = *reinterpret_cast<const float4*>(s), b = *reinterpret_cast<const float4*>(s + 4);
-    sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w;
-    sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
+  // Column c of patch half hf (k = 8 kq + 4 hf + c, rows 8 rg .. 8 rg + 7)
+  // as one 16-byte LDS write.
+  auto write_col = [&](int base, int hf, int c, const uint32_t(&col)[4]) {
+    *reinterpret_cast<u32x4*>(smem + base + swz(8 * kq + 4 * hf + c, rg)) = u32x4{col[0], col[1], col[2], col[3]};
   };
-  // Half HF of the patch, rows 4 R4 .. 4 R4 + 3: column e = 4 HF + c gets the
-  // bf16 pair (row 2q, row 2q+1) as dword q.
-#define QLORA_DX_DECODE(HF, R4, CN)                                                    \
-  {                                                                                  \
-    float f0[4], f1[4], f2[4], f3[4];                                                \
-    lut4<HF>(smem, CN[4 * (R4) + 0], f0);                                            \
-    lut4<HF>(smem, CN[4 * (R4) + 1], f1);                                            \
-    lut4<HF>(smem, CN[4 * (R4) + 2], f2);                                            \
-    lut4<HF>(smem, CN[4 * (R4) + 3], f3);                                            \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
-      col[c][2 * (R4) + 0] = pack_bf16x2(f0[c] * sc[4 * (R4) + 0], f1[c] * sc[4 * (R4) + 1]); \
-      col[c][2 * (R4) + 1] = pack_bf16x2(f2[c] * sc[4 * (R4) + 2], f3[c] * sc[4 * (R4) + 3]); \
-    }                                                                                \
-  }
-  auto write_half = [&](int base, int hf, const uint32_t(&col)[4][4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<u32x4*>(smem + base + swz(8 * kq + 4 * hf + c, rg)) =
-          u32x4{col[c][0], col[c][1], col[c][2], col[c][3]};
-  };
-  auto read_ops = [&](int wbase, int dbase, int s, bf16x8(&a)[4], bf16x8(&b)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(smem + wbase + swz(128 * wk + 32 * i + l32, 2 * s + h));
-      b[i] = *reinterpret_cast<const bf16x8*>(smem + dbase + swz(128 * wt + 32 * i + l32, 2 * s + h));
-    }
+  // MFMA operand r of a substep s: r < 4 the dY rows 128 wt + 32 r (B), else
+  // the W' rows 128 wk + 32 (r - 4) (A); lane half h takes n 8 (2s + h) ..
+  auto read_op = [&](int wbase, int dbase, int s, int r) -> bf16x8 {
+    return r < 4 ? *reinterpret_cast<const bf16x8*>(smem + dbase + swz(128 * wt + 32 * r + l32, 2 * s + h))
+                 : *reinterpret_cast<const bf16x8*>(smem + wbase + swz(128 * wk + 32 * (r - 4) + l32, 2 * s + h));
   };
 
   f32x16 acc[4][4];
@@ -174,99 +154,151 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
-  uint32_t cA[8], cB[8];   // codes, alternating steps
-  u32x4 dyr[8];            // dY rows of the next step
-  uint32_t qv;
-  float s2v;
-  float sc[8];
-  uint32_t col[4][4];
-  bf16x8 oa0[4], ob0[4], oa1[4], ob1[4];
+  uint32_t cA[8], cB[8];    // codes of two steps, alternating
+  u32x4 dyr[8];             // dY rows of the next step
+  uint32_t qv[2];           // q8 / s2 loaded one step before their scale is stored
+  float s2v[2];
+  float sc[8];              // scales of the patch being decoded
+  float fp[8][8];           // codebook values per decode unit
+  uint32_t y4[8][2], z4[8][2];
+  uint32_t col[2][4][4];    // packed columns of the two patch halves
+  bf16x8 oa[2][4], ob[2][4];
 
-  // Prologue: W'(0), dY(0) in buffers 0; scales of W(1) in table 1; codes(1)
-  // and dY(1) in the B registers.
-  load_codes(jbeg, cA);
-  load_dy(jbeg, dyr);
-  load_qs(jbeg, qv, s2v);
-  store_scale(0, qv, s2v);
-  load_qs(jbeg + 1, qv, s2v);
-  store_scale(1, qv, s2v);
-  __syncthreads();  // codebook, scale tables
-  read_scales(0, sc);
-  QLORA_DX_DECODE(0, 0, cA)
-  QLORA_DX_DECODE(0, 1, cA)
-  write_half(kW0, 0, col);
-  QLORA_DX_DECODE(1, 0, cA)
-  QLORA_DX_DECODE(1, 1, cA)
-  write_half(kW0, 1, col);
-  store_rows(kD0, dyr);
-  load_codes(jbeg + 1, cB);
-  __syncthreads();
-  read_ops(kW0, kD0, 0, oa0, ob0);
+  // The decode of W'(j+1) (codes CN) is cut into 8 units of 2 rows x 4 k:
+  // unit u = (half u >> 2, row pair u & 3).  Its 64 codebook lookups g run
+  // at slots 3g/4 (two or one per slot), its packs 4 slots after the unit's
+  // last lookup; slot U of W'(j+1) is slice U - 12 of step j (the first 12
+  // slots fall in the last slices of step j-1).  A slice is one MFMA plus
+  // its share of: operand reads for the next substep (slices 0..7 of each
+  // substep; the next step's after the barrier at slice 50), lookups, packs,
+  // column writes (half 0 at 19..22, half 1 at 43..46), dY rows to LDS
+  // (24..31) and from memory (32..39), codes of step j+2 (0..7), q8/s2 of
+  // step j+3 (8, 9), the scale of W'(j+2) (28, stored at 30) and the scale
+  // reads of W'(j+2) (56, 57).  Each slice is fenced so the issue order
+  // stays interleaved.
+#define QLORA_DX_DECODE_SLOT(U, CODES)                                                                  \
+  {                                                                                                    \
+    const int U_ = (U);                                                                                \
+    if (U_ >= 0 && U_ < 48) {                                                                          \
+      _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_) {                                               \
+        const int g_ = (4 * U_ + 2) / 3 + q_;                                                          \
+        if (g_ <= (4 * U_ + 3) / 3) {                                                                  \
+          const int u_ = g_ >> 3, e_ = g_ & 7, hf_ = u_ >> 2, pr_ = u_ & 3;                            \
+          const int row_ = 2 * pr_ + (e_ >> 2), c_ = e_ & 3;                                           \
+          if (c_ == 0) {                                                                               \
+            y4[u_][e_ >> 2] = (CODES[row_] << 2) & 0x3C3C3C3Cu;                                        \
+            z4[u_][e_ >> 2] = (CODES[row_] >> 2) & 0x3C3C3C3Cu;                                        \
+          }                                                                                            \
+          fp[u_][e_] = *reinterpret_cast<const float*>(                                                \
+              smem + bfe8((c_ & 1) ? z4[u_][e_ >> 2] : y4[u_][e_ >> 2], 2 * hf_ + (c_ >> 1)));         \
+        }                                                                                              \
+      }                                                                                                \
+    }                                                                                                  \
+    _Pragma("unroll") for (int u_ = 0; u_ < 8; ++u_) {                                                 \
+      const int c_ = U_ - (6 * u_ + 9);                                                                \
+      if (c_ >= 0 && c_ < 4) {                                                                         \
+        const int pr_ = u_ & 3;                                                                        \
+        col[u_ >> 2][c_][pr_] = pack_bf16x2(fp[u_][c_] * sc[2 * pr_], fp[u_][4 + c_] * sc[2 * pr_ + 1]); \
+      }                                                                                                \
+    }                                                                                                  \
+  }
+#define QLORA_DX_SLICE(I, MF, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                                    \
+  {                                                                                                    \
+    const int I_ = (I), s_ = I_ >> 4, i_ = I_ & 15;                                                    \
+    if (I_ == 50) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                      \
+    if (MF) acc[i_ >> 2][i_ & 3] = mfma32(oa[s_ & 1][i_ >> 2], ob[s_ & 1][i_ & 3], acc[i_ >> 2][i_ & 3]); \
+    if (s_ < 3 && i_ < 8) {                                                                            \
+      const bf16x8 v_ = read_op(WB, DB, s_ + 1, i_);                                                   \
+      if (i_ < 4) ob[(s_ + 1) & 1][i_] = v_; else oa[(s_ + 1) & 1][i_ - 4] = v_;                        \
+    }                                                                                                  \
+    if (I_ >= 50 && I_ < 58) {                                                                         \
+      const bf16x8 v_ = read_op(WN, DN, 0, I_ - 50);                                                   \
+      if (I_ - 50 < 4) ob[0][I_ - 50] = v_; else oa[0][I_ - 54] = v_;                                   \
+    }                                                                                                  \
+    if (I_ == 56 || I_ == 57) read_scales(SF, I_ - 56, sc);                                            \
+    if (I_ + 12 >= 12 && I_ + 12 < 55) QLORA_DX_DECODE_SLOT(I_ + 12, CN)                                \
+    if (I_ >= 52) QLORA_DX_DECODE_SLOT(I_ - 52, CF)                                                    \
+    if (I_ >= 19 && I_ < 23) write_col(WN, 0, I_ - 19, col[0][I_ - 19]);                                \
+    if (I_ >= 43 && I_ < 47) write_col(WN, 1, I_ - 43, col[1][I_ - 43]);                                \
+    if (I_ >= 24 && I_ < 32) store_row(DN, I_ - 24, dyr[I_ - 24]);                                     \
+    if (I_ >= 32 && I_ < 40) dyr[I_ - 32] = load_dy((J) + 2, I_ - 32);                                 \
+    if (I_ < 8) CF[I_] = load_code((J) + 2, I_);                                                       \
+    if (I_ == 8) qv[QL] = load_q((J) + 3);                                                             \
+    if (I_ == 9) s2v[QL] = load_s((J) + 3);                                                            \
+    if (I_ == 28) sfv = dq_scale(qv[QS], s2v[QS]);                                                     \
+    if (I_ == 30) *scale_slot(SF) = sfv;                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+  }
+  // Step J on buffers WB/DB (W'(J), dY(J)); WN/DN receive W'(J+1), dY(J+1);
+  // scale table SN holds W'(J+1)'s scales, SF receives W'(J+2)'s; CN holds
+  // codes(J+1), CF receives codes(J+2); q8/s2 of step J+3 go to set QL, the
+  // set QS (loaded one step earlier) gives W'(J+2)'s scale.
+#define QLORA_DX_STEP(J, I0, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                                    \
+  {                                                                                                    \
+    float sfv = 0.0f;                                                                                  \
+    auto slice_ = [&](auto ic_) __attribute__((always_inline)) {                                       \
+      constexpr int I = decltype(ic_)::value;                                                          \
+      QLORA_DX_SLICE(I, (I0) == 0, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                          \
+    };                                                                                                 \
+    run_slices<(I0)>(slice_, std::make_integer_sequence<int, 64 - (I0)>{});                            \
+    (void)sfv;                                                                                         \
+  }
 
-  // One step on buffers WB/DB (the next step's: WN/DN); the codes of step
-  // j+1 are in CN and those of step j+2 are loaded into CF; dY(j+1) is
-  // loaded at the top and written in the last substep; the scale table SN
-  // holds W(j+1)'s scales and table SF receives W(j+2)'s.
-#define QLORA_DX_MFMA(OA, OB)                                                                   \
-  _Pragma("unroll") for (int a = 0; a < 4; ++a) {                                               \
-    _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(OA[a], OB[b], acc[a][b]);  \
+  // Prologue.  W'(jbeg) and dY(jbeg) go to buffers 0 directly; the scales of
+  // W'(jbeg) and W'(jbeg+1) to tables 0 and 1; dY(jbeg+1) and the q8/s2 of
+  // jbeg+2 stay in registers.  Then the last 14 slices of a step jbeg-1
+  // read the operands of step jbeg's substep 0, the scales of W'(jbeg+1)
+  // and start its decode from codes(jbeg+1) (slices of step jbeg-1 do no
+  // loads or LDS writes).
+  {
+    uint32_t c0[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c0[i] = load_code(jbeg, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cB[i] = load_code(jbeg + 1, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dyr[i] = load_dy(jbeg, i);
+    *scale_slot(0) = dq_scale(load_q(jbeg), load_s(jbeg));
+    *scale_slot(1) = dq_scale(load_q(jbeg + 1), load_s(jbeg + 1));
+    qv[1] = load_q(jbeg + 2);
+    s2v[1] = load_s(jbeg + 2);
+    __syncthreads();  // codebook, scale tables
+    float s0[8];
+    read_scales(0, 0, s0);
+    read_scales(0, 1, s0);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t cw[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const int nib = 4 * hf + c;  // nibble of the code dword = k offset in the patch
+          const float fa = reinterpret_cast<const float*>(smem)[(c0[2 * pr] >> (4 * nib)) & 15u];
+          const float fb = reinterpret_cast<const float*>(smem)[(c0[2 * pr + 1] >> (4 * nib)) & 15u];
+          cw[pr] = pack_bf16x2(fa * s0[2 * pr], fb * s0[2 * pr + 1]);
+        }
+        write_col(kW0, hf, c, cw);
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store_row(kD0, i, dyr[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dyr[i] = load_dy(jbeg + 1, i);
+    __syncthreads();  // W'(jbeg), dY(jbeg) complete
   }
-#define QLORA_DX_SCHED(NW)                                                \
-  _Pragma("unroll") for (int i = 0; i < 16; ++i) {                        \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    \
-    if (i < (NW)) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      \
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                    \
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                    \
-  }                                                                       \
-  __builtin_amdgcn_sched_barrier(0);
-#define QLORA_DX_STEP(J, WB, DB, WN, DN, SN, SF, CN, CF)                                                    \
-  {                                                                                                        \
-    const int j_ = (J);                                                                                    \
-    /* qs first: its use later in this step then waits for no newer load */                                \
-    load_qs(j_ + 2, qv, s2v);                                                                              \
-    load_dy(j_ + 1, dyr);                                                                                  \
-    load_codes(j_ + 2, CF);                                                                                \
-    read_scales(SN, sc);                                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                                     \
-    /* substep 0: columns 0..3 of rows 0..3 of the next patch */                                           \
-    read_ops(WB, DB, 1, oa1, ob1);                                                                         \
-    QLORA_DX_MFMA(oa0, ob0)                                                                                \
-    QLORA_DX_DECODE(0, 0, CN)                                                                              \
-    QLORA_DX_SCHED(0)                                                                                      \
-    /* substep 1: columns 0..3 of rows 4..7, then those 4 columns to LDS */                                \
-    read_ops(WB, DB, 2, oa0, ob0);                                                                         \
-    QLORA_DX_MFMA(oa1, ob1)                                                                                \
-    QLORA_DX_DECODE(0, 1, CN)                                                                              \
-    write_half(WN, 0, col);                                                                                \
-    QLORA_DX_SCHED(4)                                                                                      \
-    /* substep 2: columns 4..7 of rows 0..3 */                                                             \
-    read_ops(WB, DB, 3, oa1, ob1);                                                                         \
-    QLORA_DX_MFMA(oa0, ob0)                                                                                \
-    QLORA_DX_DECODE(1, 0, CN)                                                                              \
-    QLORA_DX_SCHED(0)                                                                                      \
-    /* substep 3: columns 4..7 of rows 4..7; dY(j+1), the other patch half */                              \
-    /* and W(j+2)'s scale to their buffers */                                                              \
-    QLORA_DX_MFMA(oa1, ob1)                                                                                \
-    QLORA_DX_DECODE(1, 1, CN)                                                                              \
-    write_half(WN, 1, col);                                                                                \
-    store_rows(DN, dyr);                                                                                   \
-    store_scale(SF, qv, s2v);                                                                              \
-    QLORA_DX_SCHED(13)                                                                                     \
-    lds_barrier();                                                                                         \
-    read_ops(WN, DN, 0, oa0, ob0);                                                                         \
-  }
+  QLORA_DX_STEP(jbeg - 1, 50, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 0, 1)
 
   // Steps past jend only prefetch and decode data that is never used.
   int j = jbeg;
   for (; j + 2 <= jend; j += 2) {
-    QLORA_DX_STEP(j, kW0, kD0, kW1, kD1, 1, 0, cB, cA)
-    QLORA_DX_STEP(j + 1, kW1, kD1, kW0, kD0, 0, 1, cA, cB)
+    QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1)
+    QLORA_DX_STEP(j + 1, 0, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 1, 0)
   }
-  if (j < jend) QLORA_DX_STEP(j, kW0, kD0, kW1, kD1, 1, 0, cB, cA)
+  if (j < jend) QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1)
 #undef QLORA_DX_STEP
-#undef QLORA_DX_SCHED
-#undef QLORA_DX_DECODE
-  // Every buffer is free after the last step's barrier.
+#undef QLORA_DX_SLICE
+#undef QLORA_DX_DECODE_SLOT
+  __syncthreads();  // every wave is done with the buffers
 
   // Adapter term: A[k][j] (rows k) against the hi and lo rows of s G
   // (rows t), 64 j per pass, carried by slice 0.  The three tiles are copied
@@ -297,14 +329,23 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
       __syncthreads();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        read_ops(kW0, kD0, s, oa0, ob0);
-        QLORA_DX_MFMA(oa0, ob0)
-        read_ops(kW0, kD1, s, oa1, ob1);
-        QLORA_DX_MFMA(oa1, ob1)
+        bf16x8 av[4], bh[4], bl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          av[q] = read_op(kW0, kD0, s, 4 + q);
+          bh[q] = read_op(kW0, kD0, s, q);
+          bl[q] = read_op(kW0, kD1, s, q);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            acc[a][b] = mfma32(av[a], bh[b], acc[a][b]);
+            acc[a][b] = mfma32(av[a], bl[b], acc[a][b]);
+          }
       }
     }
   }
-#undef QLORA_DX_MFMA
 
   if (it.S > 1 && !splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats,
                                   p.counters + it.ordinal, it.S, sidx, reinterpret_cast<int*>(smem + kS0)))
