@@ -167,6 +167,49 @@ __device__ __forceinline__ void lut8_lds0(const unsigned char* lds, uint32_t x, 
   f[7] = *reinterpret_cast<const float*>(lds + bfe<24, 8>(z4));
 }
 
+// 8 * byte q of x (q = 0..3, a constant once unrolled) in one VALU
+// instruction: a shift whose source operand selects the byte (SDWA).
+template <int Q>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t x) {
+  uint32_t r;
+  if constexpr (Q == 0)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(x));
+  else if constexpr (Q == 1)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(x));
+  else if constexpr (Q == 2)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(x));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ uint32_t byte_x8(uint32_t x, int q) {
+  switch (q) {
+    case 0: return byte_x8<0>(x);
+    case 1: return byte_x8<1>(x);
+    case 2: return byte_x8<2>(x);
+    default: return byte_x8<3>(x);
+  }
+}
+
+// Pair table of the codebook at LDS address 0: entry b (b = one code byte,
+// element 2q in its low nibble) holds (c[b & 15], c[b >> 4]), so one 8-byte
+// LDS read returns the codebook values of two consecutive elements and its
+// address is 8 * b.  Built from the 16-entry codebook at `lut16` (already in
+// LDS and visible) by the workgroup's first 256 threads; the caller makes
+// the table visible with a barrier.
+__device__ __forceinline__ void pair_table_to_lds(unsigned char* lds, const float* lut16, int tid) {
+  if (tid < 256) reinterpret_cast<float2*>(lds)[tid] = make_float2(lut16[tid & 15], lut16[tid >> 4]);
+}
+// Codebook values of the 8 codes of a dword from the pair table.
+__device__ __forceinline__ void lut8_pairs(const unsigned char* lds, uint32_t x, float (&f)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float2 v = *reinterpret_cast<const float2*>(lds + byte_x8(x, q));
+    f[2 * q] = v.x;
+    f[2 * q + 1] = v.y;
+  }
+}
+
 // Workgroup barrier that waits for this wave's LDS operations only (global
 // loads stay in flight across it).  The memory clobber keeps the compiler
 // from moving memory accesses across the barrier.

@@ -19,22 +19,22 @@
 //    half h, substep s, element i covers k = 32h + 8s + i; X is read from
 //    LDS in the same permuted order, so the sum is unchanged.
 //  * Software pipeline per step (4 substeps x 16 MFMAs): during substep s the
-//    X operands of substep s+1 are read from LDS, the codebook values of
-//    chunk s of the next step's W are fetched from the LDS table, and the
-//    values fetched one substep earlier are scaled and packed to bf16 -- all
-//    interleaved between the MFMAs (one wave can hide ~6 VALU issues under a
-//    32x32x16 MFMA).  X tiles go through a 3-stage LDS ring: each lane
-//    loads its 8 x 16 bytes of the tile two steps ahead into registers and
-//    writes them to LDS one step later, so every global load has a full step
-//    to arrive before anything waits on it.  Codes are loaded two steps
-//    ahead into registers.  One barrier per step sits after substep 2, so
-//    the next step's first operand reads overlap substep 3.
+//    X operands of substep s+1 are read from LDS and chunk s of the next
+//    step's W is looked up, scaled and packed to bf16, each MFMA carrying a
+//    fixed share of that work (a substep is 16 fenced slices).  X tiles go
+//    through a 3-stage LDS ring: each lane loads its 8 x 16 bytes of the
+//    tile two steps ahead into registers and writes them to LDS one step
+//    later, so every global load has a full step to arrive before anything
+//    waits on it.  Codes are loaded two steps ahead into registers.  One
+//    barrier per step sits after substep 2, so the next step's first
+//    operand reads overlap substep 3.
 //  * X rows are 128 bytes in LDS with the 16-byte chunk index XOR-ed with
 //    bits 1..3 of the row: the 16 rows read by one 16-lane phase land in 16
 //    distinct 4-bank groups of gfx950's 64-bank LDS, and the 16 lanes of a
 //    write phase cover two adjacent rows, i.e. all 64 banks.
-//  * The codebook sits at LDS address 0, so a table lookup's address is one
-//    bitfield extract of the code byte.
+//  * The codebook is held in LDS as a 256-entry pair table at address 0:
+//    one 8-byte read per code byte returns the values of two elements, and
+//    its address is one byte-select shift of the code dword.
 //  * Ragged tiles use buffer loads, which return zero past the end.
 //  * Workgroup order is XCD-aware: each XCD works through a contiguous run of
 //    token-tile-major tiles, so an X tile is fetched into an XCD's L2 once and
@@ -50,14 +50,14 @@ namespace {
 constexpr int kTileN = 256;
 constexpr int kTileM = 256;
 constexpr int kStageBytes = kTileM * 128;  // one X stage: 256 rows x 64 bf16
-constexpr int kLutBytes = 1024;            // codebook slot (keeps stages 1 KiB aligned)
+constexpr int kLutBytes = 4096;            // pair table at 0, codebook at 2048, split ticket at 2112
 static_assert(kLutBytes + 3 * kStageBytes >= 128 * 512, "the Y staging tile fits in LDS");
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  // LDS: the codebook at address 0, then the three X stages.
+  // LDS: the codebook pair table at address 0, then the three X stages.
   __shared__ __align__(1024) unsigned char smem[kLutBytes + 3 * kStageBytes];
-  float* const lut = reinterpret_cast<float*>(smem);
+  float* const lut16 = reinterpret_cast<float*>(smem + 2048);
   unsigned char* const xring[3] = {smem + kLutBytes, smem + kLutBytes + kStageBytes,
                                    smem + kLutBytes + 2 * kStageBytes};
   const int tid = threadIdx.x;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
   const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
 
-  codebook_to_lds(lut, cb, tid);
+  codebook_to_lds(lut16, cb, tid);
 
   const int wave = tid >> 6, lane = tid & 63, ml = lane & 31, h = lane >> 5;
   const int64_t T = p.T, K = p.K, N = p.N;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
     }
   };
-  auto lut8 = [&](uint32_t x, float(&f)[8]) { lut8_lds0(smem, x, f); };
+  auto lut8 = [&](uint32_t x, float(&f)[8]) { lut8_pairs(smem, x, f); };
   auto pack8 = [&](const float(&f)[8], float sc) -> bf16x8 {
     return as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
                      pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc));
@@ -160,67 +160,65 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   u32x4 cA[2], cB[2];           // codes of the next step / the step after
   uint32_t qA[2], qB[2];
   float sA[2], sB[2];
-  bf16x8 wc[2][4], wn[2][3];    // W' operands of this step; chunks 0..2 of the next
+  bf16x8 wc[2][4], wn[2][4];    // W' operands of this step / the next
   float fp[2][8];               // codebook values of a chunk awaiting scale + pack
-  float scp[2];                 // the scales of the chunk pending in fp
   bf16x8 xa[8], xb[8];          // X operands, alternating substeps
   u32x4 xr[8];                  // X tile rows in flight from memory to LDS
 
-  // Prologue: X(0), X(1) in the ring, X(2) in registers, W(0) decoded,
-  // codes(1) in flight.
+  // Prologue: the pair table; X(0), X(1) in the ring, X(2) in registers;
+  // W(0) decoded; codes(1) and codes(2) in flight.
   load_w(kbeg, cA, qA, sA);
   load_x(kbeg, xr);
+  __syncthreads();  // the 16-entry codebook
+  pair_table_to_lds(smem, lut16, tid);
   store_x(0, xr);
   load_x(clampk(kbeg + 1), xr);
   store_x(1, xr);
   load_x(clampk(kbeg + 2), xr);
-  __syncthreads();  // lut and X(0..1) visible to every wave
+  __syncthreads();  // pair table and X(0..1) visible to every wave
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const float sc = dq_scale(qA[g], sA[g]);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int s = 0; s < 4; ++s) {
       float f[8];
       lut8(cA[g][s], f);
       wc[g][s] = pack8(f, sc);
     }
-    lut8(cA[g][3], fp[g]);  // chunk 3 of W(0) is packed in the first substep, like every step's
-    scp[g] = sc;
   }
   load_w(clampk(kbeg + 1), cA, qA, sA);
+  load_w(clampk(kbeg + 2), cB, qB, sB);
   read_x(0, 0, xa);
 
   // Substep S of a step: 16 slices, each one MFMA on (wc[.][S], XCUR) plus
   // at most one piece of each kind of side work, fenced off from the next
   // slice so the issue order stays interleaved:
   //  * slices 0..7 read X of the next substep (XNXT, ring stage RSTAGE,
-  //    chunk RS) and scale + pack one bf16 pair of the chunk pending in fp
-  //    (scales SCL) into WARR[.][WIDX];
-  //  * every slice looks up one codebook value of chunk S of the next step's
-  //    codes CA into fp (element i of slice i; a pair is packed in slice
-  //    i/2 or earlier, so the old value is consumed before it is replaced);
+  //    chunk RS) and look up one code byte of chunk S of the next step's
+  //    codes CA (two codebook values, one 8-byte read of the pair table);
+  //  * slices 8..15 scale and pack the pair looked up 8 slices earlier into
+  //    wn[.][S];
   //  * EXTRA(i) adds the step's memory traffic and scale arithmetic.
-#define QLORA_FWD_SUBSTEP(S, XCUR, XNXT, RSTAGE, RS, CA, WARR, WIDX, SCL, EXTRA)                   \
-  {                                                                                               \
-    const unsigned char* xs_ = xring[RSTAGE] + ml * 128 + (((4 * h + (RS)) ^ sw) << 4);           \
-    uint32_t y4_[2], z4_[2], pw_[2][4];                                                           \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                              \
-      acc[i & 1][i >> 1] = mfma32(wc[i & 1][S], XCUR[i >> 1], acc[i & 1][i >> 1]);                \
-      if (i < 8) {                                                                                \
-        XNXT[i] = *reinterpret_cast<const bf16x8*>(xs_ + i * 4096);                              \
-        const int g_ = i >> 2, q_ = i & 3;                                                        \
-        pw_[g_][q_] = pack_bf16x2(fp[g_][2 * q_] * SCL[g_], fp[g_][2 * q_ + 1] * SCL[g_]);        \
-        if (q_ == 3) WARR[g_][WIDX] = as_bf16x8(pw_[g_][0], pw_[g_][1], pw_[g_][2], pw_[g_][3]); \
-      }                                                                                           \
-      if ((i & 7) == 0) {                                                                         \
-        y4_[i >> 3] = (CA[i >> 3][S] << 2) & 0x3C3C3C3Cu;                                        \
-        z4_[i >> 3] = (CA[i >> 3][S] >> 2) & 0x3C3C3C3Cu;                                        \
-      }                                                                                           \
-      fp[i >> 3][i & 7] = *reinterpret_cast<const float*>(                                        \
-          smem + bfe8(((i & 1) ? z4_ : y4_)[i >> 3], (i & 7) >> 1));                              \
-      EXTRA;                                                                                      \
-      __builtin_amdgcn_sched_barrier(0);                                                          \
-    }                                                                                             \
+#define QLORA_FWD_SUBSTEP(S, XCUR, XNXT, RSTAGE, RS, CA, EXTRA)                                        \
+  {                                                                                                   \
+    const unsigned char* xs_ = xring[RSTAGE] + ml * 128 + (((4 * h + (RS)) ^ sw) << 4);               \
+    uint32_t pw_[2][4];                                                                               \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                  \
+      acc[i & 1][i >> 1] = mfma32(wc[i & 1][S], XCUR[i >> 1], acc[i & 1][i >> 1]);                    \
+      if (i < 8) {                                                                                    \
+        XNXT[i] = *reinterpret_cast<const bf16x8*>(xs_ + i * 4096);                                  \
+        const int g_ = i >> 2, q_ = i & 3;                                                            \
+        const float2 v_ = *reinterpret_cast<const float2*>(smem + byte_x8(CA[g_][S], q_));           \
+        fp[g_][2 * q_] = v_.x;                                                                        \
+        fp[g_][2 * q_ + 1] = v_.y;                                                                    \
+      } else {                                                                                        \
+        const int g_ = (i - 8) >> 2, q_ = i & 3;                                                      \
+        pw_[g_][q_] = pack_bf16x2(fp[g_][2 * q_] * sc[g_], fp[g_][2 * q_ + 1] * sc[g_]);              \
+        if (q_ == 3) wn[g_][S] = as_bf16x8(pw_[g_][0], pw_[g_][1], pw_[g_][2], pw_[g_][3]);          \
+      }                                                                                               \
+      EXTRA;                                                                                          \
+      __builtin_amdgcn_sched_barrier(0);                                                              \
+    }                                                                                                 \
   }
 
   // One pipelined step on ring stage ST (the next two steps' stages are ST1,
@@ -229,8 +227,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // loop is unrolled by six so code sets (period 2) and stages (period 3)
   // are compile-time constants: no register copies (a copy would wait for
   // the load just issued) and statically distinct LDS objects.
-  //  * substep 0 loads the codes of step kb+2 (slices 8..13) and computes
-  //    the scales of CA (slices 14, 15);
+  //  * substep 0 computes the scales of CA (slices 0, 2) and loads the codes
+  //    of step kb+2 (slices 8..13);
   //  * substep 3 moves X(kb+2) from registers to stage ST2 and reloads the
   //    registers with X(kb+3) (slices 8..15).
   // Every wave wrote its rows of X(kb+1) into ST1 one step ago; the barrier
@@ -243,23 +241,22 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     const int kn2 = (KB) + 2 < nk ? (KB) + 2 : nk - 1; /* past the end: redundant, in bounds */        \
     const int kn3 = (KB) + 3 < nk ? (KB) + 3 : nk - 1;                                                 \
     float sc[2];                                                                                       \
-    QLORA_FWD_SUBSTEP(0, xa, xb, ST, 1, CA, wc, 3, scp, {                                              \
+    QLORA_FWD_SUBSTEP(0, xa, xb, ST, 1, CA, {                                                          \
+      if (i == 0) sc[0] = dq_scale(QA[0], SA[0]);                                                      \
+      if (i == 2) sc[1] = dq_scale(QA[1], SA[1]);                                                      \
       if (i >= 8 && i < 14) load_w_part(kn2, CB, QB, SB, i - 8);                                       \
-      if (i >= 14) sc[i - 14] = dq_scale(QA[i - 14], SA[i - 14]);                                      \
     })                                                                                                 \
-    QLORA_FWD_SUBSTEP(1, xb, xa, ST, 2, CA, wn, 0, sc, {})                                             \
-    QLORA_FWD_SUBSTEP(2, xa, xb, ST, 3, CA, wn, 1, sc, {})                                             \
+    QLORA_FWD_SUBSTEP(1, xb, xa, ST, 2, CA, {})                                                        \
+    QLORA_FWD_SUBSTEP(2, xa, xb, ST, 3, CA, {})                                                        \
     asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");                                    \
-    QLORA_FWD_SUBSTEP(3, xb, xa, ST1, 0, CA, wn, 2, sc, {                                              \
+    QLORA_FWD_SUBSTEP(3, xb, xa, ST1, 0, CA, {                                                         \
       if (i >= 8) {                                                                                    \
         store_x_row(ST2, i - 8, xr[i - 8]);                                                            \
         xr[i - 8] = load_x_row(kn3, i - 8);                                                            \
       }                                                                                                \
     })                                                                                                 \
-    scp[0] = sc[0];                                                                                    \
-    scp[1] = sc[1];                                                                                    \
     _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                                    \
-      _Pragma("unroll") for (int s = 0; s < 3; ++s) wc[g][s] = wn[g][s];                              \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s) wc[g][s] = wn[g][s];                              \
     }                                                                                                  \
   }
 
@@ -348,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   if (it.S > 1) {
     __syncthreads();  // every wave is done with LDS; word 16 holds the ticket
     if (!splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats, p.counters + it.ordinal,
-                        it.S, sidx, reinterpret_cast<int*>(smem + 64)))
+                        it.S, sidx, reinterpret_cast<int*>(smem + 2112)))
       return;
   }
 
