@@ -13,8 +13,9 @@
 //    The MFMA needs 8 consecutive n per lane, but the codes run along k, so
 //    W' goes through LDS transposed ([k][n]): each thread decodes an 8 x 8
 //    patch (8 rows n, 8 k = one code dword per row) and writes 8 16-byte
-//    columns (4 k for all 8 rows at a time).  The codebook is read from LDS
-//    address 0 (one bitfield extract per lookup address).  The 8 per-row scales of a patch come from a table
+//    columns (4 k for all 8 rows at a time).  The codebook is read from a
+//    256-entry pair table at LDS address 0 (one 8-byte read per code byte,
+//    addressed by one byte-select shift).  The 8 per-row scales of a patch come from a table
 //    that the workgroup fills one step earlier, one fp64-exact scale per
 //    thread.
 //  * dY tiles are staged in LDS in their natural [t][n] layout from
@@ -49,7 +50,7 @@ namespace {
 constexpr int kTileK = 256;
 constexpr int kTileT = 256;
 constexpr int kBuf = 256 * 128;  // 256 rows x 64 bf16
-constexpr int kLut = 1024;       // codebook slot at address 0
+constexpr int kLut = 3072;       // codebook pair table at address 0, 16-entry codebook at 2048
 constexpr int kW0 = kLut, kW1 = kW0 + kBuf, kD0 = kW1 + kBuf, kD1 = kD0 + kBuf, kS0 = kD1 + kBuf;
 constexpr int kSBytes = 4 * 64 * 4;  // [4 k-blocks][64 rows] fp32 scales
 constexpr int kSmem = kS0 + 2 * kSBytes;
@@ -82,7 +83,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // built from them must be uniform).
   const int tk = __builtin_amdgcn_readfirstlane(tile / p.tiles_t);
   const int tt = __builtin_amdgcn_readfirstlane(tile % p.tiles_t);
-  codebook_to_lds(reinterpret_cast<float*>(smem), cb, tid);
+  const float* const lut16 = reinterpret_cast<const float*>(smem + 2048);
+  codebook_to_lds(reinterpret_cast<float*>(smem + 2048), cb, tid);
 
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wk = wave & 1, wt = wave >> 1;
@@ -160,15 +162,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   float s2v[2];
   float sc[8];              // scales of the patch being decoded
   float fp[8][8];           // codebook values per decode unit
-  uint32_t y4[8][2], z4[8][2];
   uint32_t col[2][4][4];    // packed columns of the two patch halves
   bf16x8 oa[2][4], ob[2][4];
 
   // The decode of W'(j+1) (codes CN) is cut into 8 units of 2 rows x 4 k:
-  // unit u = (half u >> 2, row pair u & 3).  Its 64 codebook lookups g run
-  // at slots 3g/4 (two or one per slot), its packs 4 slots after the unit's
-  // last lookup; slot U of W'(j+1) is slice U - 12 of step j (the first 12
-  // slots fall in the last slices of step j-1).  A slice is one MFMA plus
+  // unit u = (half u >> 2, row pair u & 3).  Its 32 lookups g of the pair
+  // table (two codebook values each) run at slots 3g/2, its packs 4 slots
+  // after the unit's last lookup; slot U of W'(j+1) is slice U - 12 of step
+  // j (the first 12 slots fall in the last slices of step j-1).  A slice is
+  // one MFMA plus
   // its share of: operand reads for the next substep (slices 0..7 of each
   // substep; the next step's after the barrier at slice 50), lookups, packs,
   // column writes (half 0 at 19..22, half 1 at 43..46), dY rows to LDS
@@ -179,23 +181,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
 #define QLORA_DX_DECODE_SLOT(U, CODES)                                                                  \
   {                                                                                                    \
     const int U_ = (U);                                                                                \
-    if (U_ >= 0 && U_ < 48) {                                                                          \
-      _Pragma("unroll") for (int q_ = 0; q_ < 2; ++q_) {                                               \
-        const int g_ = (4 * U_ + 2) / 3 + q_;                                                          \
-        if (g_ <= (4 * U_ + 3) / 3) {                                                                  \
-          const int u_ = g_ >> 3, e_ = g_ & 7, hf_ = u_ >> 2, pr_ = u_ & 3;                            \
-          const int row_ = 2 * pr_ + (e_ >> 2), c_ = e_ & 3;                                           \
-          if (c_ == 0) {                                                                               \
-            y4[u_][e_ >> 2] = (CODES[row_] << 2) & 0x3C3C3C3Cu;                                        \
-            z4[u_][e_ >> 2] = (CODES[row_] >> 2) & 0x3C3C3C3Cu;                                        \
-          }                                                                                            \
-          fp[u_][e_] = *reinterpret_cast<const float*>(                                                \
-              smem + bfe8((c_ & 1) ? z4[u_][e_ >> 2] : y4[u_][e_ >> 2], 2 * hf_ + (c_ >> 1)));         \
-        }                                                                                              \
-      }                                                                                                \
+    const int g_ = (2 * U_ + 2) / 3;                                                                   \
+    if (U_ >= 0 && g_ < 32 && (3 * g_) / 2 == U_) {                                                    \
+      const int u_ = g_ >> 2, w_ = g_ & 3, hf_ = u_ >> 2, pr_ = u_ & 3;                                \
+      const int rs_ = w_ >> 1, b_ = w_ & 1;                                                            \
+      const float2 v_ = *reinterpret_cast<const float2*>(smem + byte_x8(CODES[2 * pr_ + rs_], 2 * hf_ + b_)); \
+      fp[u_][4 * rs_ + 2 * b_] = v_.x;                                                                 \
+      fp[u_][4 * rs_ + 2 * b_ + 1] = v_.y;                                                             \
     }                                                                                                  \
     _Pragma("unroll") for (int u_ = 0; u_ < 8; ++u_) {                                                 \
-      const int c_ = U_ - (6 * u_ + 9);                                                                \
+      const int c_ = U_ - (6 * u_ + 8);                                                                \
       if (c_ >= 0 && c_ < 4) {                                                                         \
         const int pr_ = u_ & 3;                                                                        \
         col[u_ >> 2][c_][pr_] = pack_bf16x2(fp[u_][c_] * sc[2 * pr_], fp[u_][4 + c_] * sc[2 * pr_ + 1]); \
@@ -216,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
       if (I_ - 50 < 4) ob[0][I_ - 50] = v_; else oa[0][I_ - 54] = v_;                                   \
     }                                                                                                  \
     if (I_ == 56 || I_ == 57) read_scales(SF, I_ - 56, sc);                                            \
-    if (I_ + 12 >= 12 && I_ + 12 < 55) QLORA_DX_DECODE_SLOT(I_ + 12, CN)                                \
+    if (I_ + 12 >= 12 && I_ + 12 < 54) QLORA_DX_DECODE_SLOT(I_ + 12, CN)                                \
     if (I_ >= 52) QLORA_DX_DECODE_SLOT(I_ - 52, CF)                                                    \
     if (I_ >= 19 && I_ < 23) write_col(WN, 0, I_ - 19, col[0][I_ - 19]);                                \
     if (I_ >= 43 && I_ < 47) write_col(WN, 1, I_ - 43, col[1][I_ - 43]);                                \
@@ -263,6 +258,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
     qv[1] = load_q(jbeg + 2);
     s2v[1] = load_s(jbeg + 2);
     __syncthreads();  // codebook, scale tables
+    pair_table_to_lds(smem, lut16, tid);  // visible after the prologue's second barrier
     float s0[8];
     read_scales(0, 0, s0);
     read_scales(0, 1, s0);
@@ -274,8 +270,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
           const int nib = 4 * hf + c;  // nibble of the code dword = k offset in the patch
-          const float fa = reinterpret_cast<const float*>(smem)[(c0[2 * pr] >> (4 * nib)) & 15u];
-          const float fb = reinterpret_cast<const float*>(smem)[(c0[2 * pr + 1] >> (4 * nib)) & 15u];
+          const float fa = lut16[(c0[2 * pr] >> (4 * nib)) & 15u];
+          const float fb = lut16[(c0[2 * pr + 1] >> (4 * nib)) & 15u];
           cw[pr] = pack_bf16x2(fa * s0[2 * pr], fb * s0[2 * pr + 1]);
         }
         write_col(kW0, hf, c, cw);
