@@ -170,14 +170,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // table (two codebook values each) run at slots 3g/2, its packs 4 slots
   // after the unit's last lookup; slot U of W'(j+1) is slice U - 12 of step
   // j (the first 12 slots fall in the last slices of step j-1).  A slice is
-  // one MFMA plus
-  // its share of: operand reads for the next substep (slices 0..7 of each
-  // substep; the next step's after the barrier at slice 50), lookups, packs,
-  // column writes (half 0 at 19..22, half 1 at 43..46), dY rows to LDS
-  // (24..31) and from memory (32..39), codes of step j+2 (0..7), q8/s2 of
-  // step j+3 (8, 9), the scale of W'(j+2) (28, stored at 30) and the scale
-  // reads of W'(j+2) (56, 57).  Each slice is fenced so the issue order
-  // stays interleaved.
+  // one MFMA plus its share of: operand reads for the next substep (slices
+  // 0..7 of each substep; the next step's after the barrier at slice 50),
+  // lookups, packs, column writes (half 0 at 19..22, half 1 at 43..46), dY
+  // rows to LDS (24..31) and from memory (32..39), codes of step j+2
+  // (0..7), q8/s2 of step j+3 (8, 9), the scale of W'(j+2) (28, stored at
+  // 30) and the scale reads of W'(j+2) (56, 57).  Each slice is fenced so
+  // the issue order stays interleaved.
 #define QLORA_DX_DECODE_SLOT(U, CODES)                                                                  \
   {                                                                                                    \
     const int U_ = (U);                                                                                \
