@@ -107,14 +107,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Raw buffer descriptors: loads at offsets at or past `bytes` return zero, so
-// ragged tile edges need no branches.  Offsets are 32-bit, relative to base.
+// ragged tile edges need no branches.  Offsets are 32-bit, relative to base;
+// kOffNone is past every view (a masked lane loads zero without a branch).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOffNone = 0x7FFFFF00u;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);

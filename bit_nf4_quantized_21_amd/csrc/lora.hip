@@ -83,28 +83,30 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
     u32x4 v[JB][4];   // V_LR == false: the operands themselves
     uint2 a[JB][8];   // V_LR: 8 rows x 4 columns per j-block, transposed at use
   };
+  // Buffer views (this workgroup's rows of M; all of V): masked lanes load
+  // zero through an offset past the view, so the loads carry no branches and
+  // the next step's loads stay in flight while this step computes.
+  const int64_t rows = T - t0 < 64 ? T - t0 : 64;
+  const rsrc_t rm = make_rsrc(M + t0 * L, rows * L * 2);
+  const rsrc_t rv = make_rsrc(V, (int64_t)r * L * 2);
   auto load = [&](int s, Regs& R) {
     const int64_t l = wl0 + 32 * s + 8 * g;
     const bool lv = l < wl1;  // L % 8 == 0: an 8-group is whole or absent
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int64_t t = t0 + 16 * tt + p;
-      R.m[tt] = (lv && t < T) ? *reinterpret_cast<const u32x4*>(M + t * L + l) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int tt = 0; tt < 4; ++tt)
+      R.m[tt] = buf_load16(rm, lv ? (uint32_t)(((16 * tt + p) * L + l) * 2) : kOffNone);
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       if constexpr (V_LR) {
         const int j = 64 * jb + 4 * p;
         const bool ok = lv && j < r;  // r % 8 == 0: a 4-group is whole or absent
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          R.a[jb][i] = ok ? *reinterpret_cast<const uint2*>(V + (l + i) * r + j) : make_uint2(0u, 0u);
+        for (int i = 0; i < 8; ++i) R.a[jb][i] = buf_load8(rv, ok ? (uint32_t)(((l + i) * r + j) * 2) : kOffNone);
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j = 64 * jb + 4 * p + c;
-          R.v[jb][c] = (lv && j < r) ? *reinterpret_cast<const u32x4*>(V + (int64_t)j * L + l)
-                                     : u32x4{0u, 0u, 0u, 0u};
+          R.v[jb][c] = buf_load16(rv, (lv && j < r) ? (uint32_t)((j * L + l) * 2) : kOffNone);
         }
       }
     }
@@ -312,11 +314,14 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
     uint2 a[8];
     u32x4 h[JT], l[JT];
   };
+  // M viewed from this chunk's first token: masked lanes (m past C, t past
+  // this wave's range) load zero through an offset past the view.
+  const rsrc_t rm = make_rsrc(M + tbeg * C, (tend - tbeg) * C * 2);
   auto load = [&](int s, Regs& R) {
     const int64_t t = wt0 + 32 * s + 8 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      R.a[i] = (mv && t + i < wt1) ? *reinterpret_cast<const uint2*>(M + (t + i) * C + m) : make_uint2(0u, 0u);
+      R.a[i] = buf_load8(rm, (mv && t + i < wt1) ? (uint32_t)(((t + i - tbeg) * C + m) * 2) : kOffNone);
     // The planes are zero for t >= T and hold TP >= T columns, so the loads
     // need no token mask; steps past this wave's range are masked via M.
 #pragma unroll
