@@ -51,15 +51,16 @@ constexpr int kTileN = 256;
 constexpr int kTileM = 256;
 constexpr int kStageBytes = kTileM * 128;  // one X stage: 256 rows x 64 bf16
 constexpr int kLutBytes = 4096;            // pair table at 0, codebook at 2048, split ticket at 2112
-static_assert(kLutBytes + 3 * kStageBytes >= 128 * 512, "the Y staging tile fits in LDS");
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  // LDS: the codebook pair table at address 0, then the three X stages.
-  __shared__ __align__(1024) unsigned char smem[kLutBytes + 3 * kStageBytes];
-  float* const lut16 = reinterpret_cast<float*>(smem + 2048);
-  unsigned char* const xring[3] = {smem + kLutBytes, smem + kLutBytes + kStageBytes,
-                                   smem + kLutBytes + 2 * kStageBytes};
+  // LDS: the codebook pair table (with the 16-entry codebook and the split
+  // ticket after it) and four X stages, each its own object so the compiler
+  // can tell a stage being filled by buffer-to-LDS loads from the ones read.
+  __shared__ __align__(4096) unsigned char tbl[kLutBytes];
+  __shared__ __align__(1024) unsigned char xs0[kStageBytes], xs1[kStageBytes], xs2[kStageBytes], xs3[kStageBytes];
+  float* const lut16 = reinterpret_cast<float*>(tbl + 2048);
+  unsigned char* const xring[4] = {xs0, xs1, xs2, xs3};
   const int tid = threadIdx.x;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tiles are ordered
@@ -95,25 +96,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     nval[g] = n0 + nl[g] < N;
   }
 
-  // X staging: wave w moves rows [64w, 64w+64) of a stage, 8 rows per
-  // instruction; lane l covers row 64w + 8j + l/8, logical chunk l%8, stored
-  // at physical chunk (l%8) ^ ((row >> 1) & 7).
+  // X staging by buffer-to-LDS loads: wave w fills rows [64w, 64w+64) of a
+  // stage, 8 rows per instruction; lane l writes physical chunk l%8 of row
+  // 64w + 8j + l/8 with the logical chunk (l%8) ^ ((row >> 1) & 7) of X.
   const int dr = lane >> 3, dpc = lane & 7;
-  const uint32_t xg = (uint32_t)((64 * wave + dr) * K * 2 + dpc * 16);
-  const uint32_t xl_even = (uint32_t)((64 * wave + dr) * 128 + ((dpc ^ (dr >> 1)) << 4));
-  const uint32_t xl_odd = (uint32_t)((64 * wave + dr) * 128 + ((dpc ^ ((dr >> 1) | 4)) << 4));
-  auto load_x = [&](int kb, u32x4(&xr)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xr[j] = buf_load16(rx, xg + (uint32_t)(8 * j * K * 2 + kb * 128));
-  };
-  auto store_x = [&](int stage, const u32x4(&xr)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(xring[stage] + ((j & 1) ? xl_odd : xl_even) + 8 * j * 128) = xr[j];
-  };
-  auto load_x_row = [&](int kb, int j) -> u32x4 { return buf_load16(rx, xg + (uint32_t)(8 * j * K * 2 + kb * 128)); };
-  auto store_x_row = [&](int stage, int j, const u32x4& v) {
-    *reinterpret_cast<u32x4*>(xring[stage] + ((j & 1) ? xl_odd : xl_even) + 8 * j * 128) = v;
+  const uint32_t xg_even = (uint32_t)((64 * wave + dr) * K * 2 + ((dpc ^ (dr >> 1)) << 4));
+  const uint32_t xg_odd = (uint32_t)((64 * wave + dr) * K * 2 + ((dpc ^ ((dr >> 1) | 4)) << 4));
+  auto dma_x_row = [&](int stage, int kb, int j) {
+    buf_load16_to_lds(rx, xring[stage] + (64 * wave + 8 * j) * 128,
+                      ((j & 1) ? xg_odd : xg_even) + (uint32_t)(8 * j * K * 2 + kb * 128));
   };
   // One of the six loads of load_w: part 3g + {0: codes, 1: q8, 2: s2}.
   auto load_w_part = [&](int kb, u32x4(&c)[2], uint32_t(&q)[2], float(&sv)[2], int part) {
@@ -136,7 +127,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       sv[g] = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
     }
   };
-  auto lut8 = [&](uint32_t x, float(&f)[8]) { lut8_pairs(smem, x, f); };
+  auto lut8 = [&](uint32_t x, float(&f)[8]) { lut8_pairs(tbl, x, f); };
   auto pack8 = [&](const float(&f)[8], float sc) -> bf16x8 {
     return as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
                      pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc));
@@ -163,18 +154,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   bf16x8 wc[2][4], wn[2][4];    // W' operands of this step / the next
   float fp[2][8];               // codebook values of a chunk awaiting scale + pack
   bf16x8 xa[8], xb[8];          // X operands, alternating substeps
-  u32x4 xr[8];                  // X tile rows in flight from memory to LDS
 
-  // Prologue: the pair table; X(0), X(1) in the ring, X(2) in registers;
-  // W(0) decoded; codes(1) and codes(2) in flight.
+  // Prologue: the pair table; X(0), X(1) in stages 0, 1; W(0) decoded;
+  // then codes(1) and X(2) in flight, issued in the order the loop issues
+  // them (codes, then a stage), so the wait counts at the loop top that
+  // hold for the first pass hold for every pass.
   load_w(kbeg, cA, qA, sA);
-  load_x(kbeg, xr);
-  __syncthreads();  // the 16-entry codebook
-  pair_table_to_lds(smem, lut16, tid);
-  store_x(0, xr);
-  load_x(clampk(kbeg + 1), xr);
-  store_x(1, xr);
-  load_x(clampk(kbeg + 2), xr);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    dma_x_row(0, kbeg, j);
+    dma_x_row(1, clampk(kbeg + 1), j);
+  }
+  __syncthreads();  // the 16-entry codebook (and this wave's loads have landed)
+  pair_table_to_lds(tbl, lut16, tid);
   __syncthreads();  // pair table and X(0..1) visible to every wave
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -186,8 +178,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       wc[g][s] = pack8(f, sc);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
   load_w(clampk(kbeg + 1), cA, qA, sA);
-  load_w(clampk(kbeg + 2), cB, qB, sB);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_x_row(2, clampk(kbeg + 2), j);
+  __builtin_amdgcn_sched_barrier(0);
   read_x(0, 0, xa);
 
   // Substep S of a step: 16 slices, each one MFMA on (wc[.][S], XCUR) plus
@@ -208,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
       if (i < 8) {                                                                                    \
         XNXT[i] = *reinterpret_cast<const bf16x8*>(xs_ + i * 4096);                                  \
         const int g_ = i >> 2, q_ = i & 3;                                                            \
-        const float2 v_ = *reinterpret_cast<const float2*>(smem + byte_x8(CA[g_][S], q_));           \
+        const float2 v_ = *reinterpret_cast<const float2*>(tbl + byte_x8(CA[g_][S], q_));            \
         fp[g_][2 * q_] = v_.x;                                                                        \
         fp[g_][2 * q_ + 1] = v_.y;                                                                    \
       } else {                                                                                        \
@@ -221,22 +217,22 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     }                                                                                                 \
   }
 
-  // One pipelined step on ring stage ST (the next two steps' stages are ST1,
-  // ST2).  CA.. name the register set holding the codes of step kb+1
+  // One pipelined step; X(kb) is in ring stage ST, X(kb+1) in ST1, and
+  // stage ST3 (X(kb-1)'s, read for the last time in step kb-1) receives
+  // X(kb+3).  CA.. name the register set holding the codes of step kb+1
   // (decoded now), CB.. the set that receives the codes of step kb+2.  The
-  // loop is unrolled by six so code sets (period 2) and stages (period 3)
+  // loop is unrolled by four so code sets (period 2) and stages (period 4)
   // are compile-time constants: no register copies (a copy would wait for
   // the load just issued) and statically distinct LDS objects.
   //  * substep 0 computes the scales of CA (slices 0, 2) and loads the codes
   //    of step kb+2 (slices 8..13);
-  //  * substep 3 moves X(kb+2) from registers to stage ST2 and reloads the
-  //    registers with X(kb+3) (slices 8..15).
-  // Every wave wrote its rows of X(kb+1) into ST1 one step ago; the barrier
-  // before substep 3 makes them visible before substep 3 reads them, and
-  // every wave is done with stage ST2 (last read in step kb-1) by then.  At
-  // most 8 of this wave's LDS operations are left in flight across it: the
-  // stage writes are older than the last 8.
-#define QLORA_FWD_STEP(KB, ST, ST1, ST2, CA, QA, SA, CB, QB, SB)                                       \
+  //  * substep 3 loads X(kb+3) into stage ST3 (slices 8..15).
+  // The barrier before substep 3 publishes X(kb+1), loaded two steps ago:
+  // each wave first waits for its own loads of that step (20 buffer
+  // operations were issued after them) and leaves at most 8 LDS operations
+  // in flight; after the barrier every wave is also done with step kb-1,
+  // so stage ST3 is free.
+#define QLORA_FWD_STEP(KB, ST, ST1, ST3, CA, QA, SA, CB, QB, SB)                                       \
   {                                                                                                    \
     const int kn2 = (KB) + 2 < nk ? (KB) + 2 : nk - 1; /* past the end: redundant, in bounds */        \
     const int kn3 = (KB) + 3 < nk ? (KB) + 3 : nk - 1;                                                 \
@@ -248,36 +244,29 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     })                                                                                                 \
     QLORA_FWD_SUBSTEP(1, xb, xa, ST, 2, CA, {})                                                        \
     QLORA_FWD_SUBSTEP(2, xa, xb, ST, 3, CA, {})                                                        \
-    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");                                    \
+    asm volatile("s_waitcnt vmcnt(20) lgkmcnt(8)\n\ts_barrier" ::: "memory");                         \
     QLORA_FWD_SUBSTEP(3, xb, xa, ST1, 0, CA, {                                                         \
-      if (i >= 8) {                                                                                    \
-        store_x_row(ST2, i - 8, xr[i - 8]);                                                            \
-        xr[i - 8] = load_x_row(kn3, i - 8);                                                            \
-      }                                                                                                \
+      if (i >= 8) dma_x_row(ST3, kn3, i - 8);                                                          \
     })                                                                                                 \
     _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                                    \
       _Pragma("unroll") for (int s = 0; s < 4; ++s) wc[g][s] = wn[g][s];                              \
     }                                                                                                  \
   }
 
-  // Whole groups of six steps loop; the remainder runs once after the loop,
+  // Whole groups of four steps loop; the remainder runs once after the loop,
   // so the loop back-edge is reached from one path only and the wait counts
   // at its top stay exact.
   int kb = kbeg;
-  for (; kb + 6 <= kend; kb += 6) {
-    QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
+  for (; kb + 4 <= kend; kb += 4) {
+    QLORA_FWD_STEP(kb, 0, 1, 3, cA, qA, sA, cB, qB, sB)
     QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
-    QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
-    QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
-    QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
-    QLORA_FWD_STEP(kb + 5, 2, 0, 1, cB, qB, sB, cA, qA, sA)
+    QLORA_FWD_STEP(kb + 2, 2, 3, 1, cA, qA, sA, cB, qB, sB)
+    QLORA_FWD_STEP(kb + 3, 3, 0, 2, cB, qB, sB, cA, qA, sA)
   }
   if (kb < kend) {
-    QLORA_FWD_STEP(kb, 0, 1, 2, cA, qA, sA, cB, qB, sB)
+    QLORA_FWD_STEP(kb, 0, 1, 3, cA, qA, sA, cB, qB, sB)
     if (kb + 1 < kend) QLORA_FWD_STEP(kb + 1, 1, 2, 0, cB, qB, sB, cA, qA, sA)
-    if (kb + 2 < kend) QLORA_FWD_STEP(kb + 2, 2, 0, 1, cA, qA, sA, cB, qB, sB)
-    if (kb + 3 < kend) QLORA_FWD_STEP(kb + 3, 0, 1, 2, cB, qB, sB, cA, qA, sA)
-    if (kb + 4 < kend) QLORA_FWD_STEP(kb + 4, 1, 2, 0, cA, qA, sA, cB, qB, sB)
+    if (kb + 2 < kend) QLORA_FWD_STEP(kb + 2, 2, 3, 1, cA, qA, sA, cB, qB, sB)
   }
 #undef QLORA_FWD_STEP
 #undef QLORA_FWD_SUBSTEP
@@ -345,39 +334,38 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   if (it.S > 1) {
     __syncthreads();  // every wave is done with LDS; word 16 holds the ticket
     if (!splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats, p.counters + it.ordinal,
-                        it.S, sidx, reinterpret_cast<int*>(smem + 2112)))
+                        it.S, sidx, reinterpret_cast<int*>(tbl + 2112)))
       return;
   }
 
-  // Y through LDS, 128 token rows at a time: D[n][m] of a 32x32 tile gives
-  // lane (ml, h) token m = 32 mi + ml and the 4 features 8 q4 + 4h + (0..3),
-  // written as bf16 into a [128 m][256 n] tile whose 16-byte chunks are
-  // XOR-swizzled by the row (the 32 lanes of a write land in 32 distinct
-  // chunks); then each 32 lanes store one whole 512-byte row of Y.
+  // Y through LDS: D[n][m] of a 32x32 tile gives lane (ml, h) token
+  // m = 32 mi + ml and the 4 features 8 q4 + 4h + (0..3), written as bf16
+  // into [64 m][256 n] tiles (stage q holds token rows 64q .. 64q + 63)
+  // whose 16-byte chunks are XOR-swizzled by the row (the 32 lanes of a
+  // write land in 32 distinct chunks); then each 32 lanes store one whole
+  // 512-byte row of Y.
+  __syncthreads();  // every wave is done with the stages
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();  // the stages (or the previous half) are free
+  for (int mi = 0; mi < 8; ++mi) {
+    unsigned char* const yst = xring[mi >> 1];
+    const int row = 32 * (mi & 1) + ml;
 #pragma unroll
-    for (int mq = 0; mq < 4; ++mq) {
-      const int mi = 4 * half + mq, row = 32 * mq + ml;
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = 8 * wave + 4 * g + q4;
+        const f32x16& a = acc[g][mi];
+        *reinterpret_cast<uint2*>(yst + row * 512 + ((c ^ ml) << 4) + 8 * h) =
+            make_uint2(pack_bf16x2(a[4 * q4 + 0], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3]));
+      }
+  }
+  __syncthreads();
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = 8 * wave + 4 * g + q4;
-          const f32x16& a = acc[g][mi];
-          *reinterpret_cast<uint2*>(smem + row * 512 + ((c ^ ml) << 4) + 8 * h) =
-              make_uint2(pack_bf16x2(a[4 * q4 + 0], a[4 * q4 + 1]), pack_bf16x2(a[4 * q4 + 2], a[4 * q4 + 3]));
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;
-      const int64_t m = m0 + 128 * half + row, n = n0 + 8 * c;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * 512 + ((c ^ (row & 31)) << 4));
-      if (m < T && n < N) *reinterpret_cast<u32x4*>(p.Y + m * N + n) = v;  // N % 8 == 0: chunks whole
-    }
+  for (int i = 0; i < 32; ++i) {
+    const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;  // row 0..255 = 64 * (i / 8) + ..
+    const int64_t m = m0 + row, n = n0 + 8 * c;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xring[i >> 3] + (row & 63) * 512 + ((c ^ (row & 31)) << 4));
+    if (m < T && n < N) *reinterpret_cast<u32x4*>(p.Y + m * N + n) = v;  // N % 8 == 0: chunks whole
   }
 }
 
