@@ -6,6 +6,12 @@
 // last ticket sums the S slots in slot order (its own from registers), so the
 // result does not depend on which slice finished last, and resets the
 // counter to zero for the next launch.  Nothing waits on another workgroup.
+//
+// The slots and the counter are accessed with system-scope cache policy
+// (stores and loads that no XCD's caches keep, atomics at the coherence
+// point), so the hand-off holds wherever the slices run, and no cache has to
+// be written back or invalidated: a device-scope fence would write back and
+// invalidate the whole L2 of the XCD, which stalls every workgroup on it.
 #pragma once
 
 #include "common.hpp"
@@ -13,6 +19,7 @@
 namespace qlora {
 
 constexpr int kSplitSlotFloats = 256 * 256;  // one tile of fp32 partials
+constexpr int kCachePolicySystem = 1 | 16;   // sc0 | sc1
 
 // Returns true in the workgroup that must finish the tile (acc then holds the
 // full sum); false in the others, which must exit without storing.  Called by
@@ -22,42 +29,55 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
                                                int S, int sidx, int* flag) {
   static_assert(NA * NB * 16 * NT == kSplitSlotFloats, "tile size");
   const int tid = threadIdx.x;
-  float4* mine = reinterpret_cast<float4*>(slots) + (int64_t)sidx * (kSplitSlotFloats / 4);
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        mine[((a * NB + b) * 4 + e4) * NT + tid] =
-            make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]);
-  __threadfence();  // this slot is visible device-wide before the ticket
-  __syncthreads();
-  if (tid == 0) *flag = atomicAdd(counter, 1);
-  __syncthreads();
-  if (*flag != S - 1) return false;
-  __threadfence();  // acquire: the other slots are complete
+  const rsrc_t rs = make_rsrc(slots, (int64_t)S * kSplitSlotFloats * 4);
+  const uint32_t mine = (uint32_t)sidx * kSplitSlotFloats * 4;
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t idx = ((a * NB + b) * 4 + e4) * NT + tid;
-        const float4 own = make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2],
-                                       acc[a][b][4 * e4 + 3]);
-        const float4* sl = reinterpret_cast<const float4*>(slots);
-        float4 sum = sidx == 0 ? own : sl[idx];
-        for (int s = 1; s < S; ++s) {
-          const float4 v = s == sidx ? own : sl[(int64_t)s * (kSplitSlotFloats / 4) + idx];
-          sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        const uint32_t off = (uint32_t)((((a * NB + b) * 4 + e4) * NT + tid) * 16);
+        const u32x4 v = u32x4{__float_as_uint(acc[a][b][4 * e4]), __float_as_uint(acc[a][b][4 * e4 + 1]),
+                              __float_as_uint(acc[a][b][4 * e4 + 2]), __float_as_uint(acc[a][b][4 * e4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                               rs, (int)(mine + off), 0, kCachePolicySystem);
+      }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's slot stores are complete
+  __syncthreads();
+  if (tid == 0) *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  if (*flag != S - 1) return false;
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const uint32_t off = (uint32_t)((((a * NB + b) * 4 + e4) * NT + tid) * 16);
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < S; ++s) {
+          float4 v;
+          if (s == sidx) {
+            v = make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]);
+          } else {
+            const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rs, (int)((uint32_t)s * kSplitSlotFloats * 4 + off), 0,
+                                                          kCachePolicySystem));
+            v = make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3]));
+          }
+          if (s == 0) {
+            sum = v;
+          } else {
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+          }
         }
         acc[a][b][4 * e4] = sum.x;
         acc[a][b][4 * e4 + 1] = sum.y;
         acc[a][b][4 * e4 + 2] = sum.z;
         acc[a][b][4 * e4 + 3] = sum.w;
       }
-  if (tid == 0) atomicExch(counter, 0);
+  if (tid == 0) __hip_atomic_exchange(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return true;
 }
 
