@@ -115,6 +115,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
+// `off` where ok, else kOffNone, without a branch: the lane mask passes
+// through an empty asm, so the optimizer cannot turn the choice back into
+// control flow around the load that uses it.
+__device__ __forceinline__ uint32_t off_if(bool ok, uint32_t off) {
+  uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return (off & m) | (kOffNone & ~m);
+}
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }

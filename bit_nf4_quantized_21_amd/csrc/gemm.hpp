@@ -23,7 +23,7 @@ struct FwdGemmParams {
   int r, RP;             // RP = r rounded up to 64
   float s;
   float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
-  int* counters;         // one per split tile, zero on entry, left zero
+  int* counters;         // 2 per split tile (tickets, then published counts), zero on entry, left zero
   SplitPlan plan;        // filled by the launcher
   int tiles_n, tiles_m;  // filled by the launcher
 };
@@ -40,7 +40,7 @@ struct DxGemmParams {
   int64_t T, K, N;
   int r, RP;            // RP = r rounded up to 64
   float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
-  int* counters;         // one per split tile, zero on entry, left zero
+  int* counters;         // 2 per split tile (tickets, then published counts), zero on entry, left zero
   SplitPlan plan;        // filled by the launcher
   int tiles_k, tiles_t;
 };

@@ -334,6 +334,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   if (it.S > 1) {
     __syncthreads();  // every wave is done with LDS; word 16 holds the ticket
     if (!splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats, p.counters + it.ordinal,
+                        p.counters + p.plan.nsplit() + it.ordinal,
                         it.S, sidx, reinterpret_cast<int*>(tbl + 2112)))
       return;
   }

@@ -67,7 +67,7 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   l.ptok = align256(pdb > pda ? pdb : pda);
   const SplitPlan dp = dx_plan(T, K, N);
   l.slots = dp.S > 1 ? align256((size_t)dp.nsplit() * dp.S * kSplitSlotFloats * sizeof(float)) : 0;
-  l.counters = align256((size_t)(dp.nsplit() > 0 ? dp.nsplit() : 1) * sizeof(int));
+  l.counters = align256((size_t)(dp.nsplit() > 0 ? 2 * dp.nsplit() : 1) * sizeof(int));
   l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok + l.slots + l.counters;
   return l;
 }
@@ -86,7 +86,7 @@ FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
     l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
     l.g = fwd_plan(T, K, N);
     l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
-    l.counters = align256((size_t)(l.g.nsplit() > 0 ? l.g.nsplit() : 1) * sizeof(int));
+    l.counters = align256((size_t)(l.g.nsplit() > 0 ? 2 * l.g.nsplit() : 1) * sizeof(int));
   }
   l.total = l.p + 2 * l.xah + l.slots + l.counters;
   return l;
@@ -118,7 +118,7 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
     o.row_lo = XAl;
     o.scale_row = a.s;
     o.zero = reinterpret_cast<int*>(w2 + l.slots);  // the GEMM's split tickets
-    o.nzero = l.g.nsplit();
+    o.nzero = 2 * l.g.nsplit();
   }
   hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
   if (e != hipSuccess) return e;
@@ -179,7 +179,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   o.side_hi = XAth;
   o.side_lo = XAtl;
   o.zero = counters;  // the dX GEMM's split tickets
-  o.nzero = dp.nsplit();
+  o.nzero = 2 * dp.nsplit();
   hipError_t e = launch_rowdot(dY, a.B, /*v_lr=*/false, Pg, o, a.T, a.N, a.r, row_chunk(a.T, a.N), s);
   if (e != hipSuccess) return e;
   e = launch_tokdot(dY, XAth, XAtl, TP, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*m_major=*/false, s);

@@ -94,19 +94,19 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
     const bool lv = l < wl1;  // L % 8 == 0: an 8-group is whole or absent
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
-      R.m[tt] = buf_load16(rm, lv ? (uint32_t)(((16 * tt + p) * L + l) * 2) : kOffNone);
+      R.m[tt] = buf_load16(rm, off_if(lv, (uint32_t)(((16 * tt + p) * L + l) * 2)));
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       if constexpr (V_LR) {
         const int j = 64 * jb + 4 * p;
         const bool ok = lv && j < r;  // r % 8 == 0: a 4-group is whole or absent
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R.a[jb][i] = buf_load8(rv, ok ? (uint32_t)(((l + i) * r + j) * 2) : kOffNone);
+        for (int i = 0; i < 8; ++i) R.a[jb][i] = buf_load8(rv, off_if(ok, (uint32_t)(((l + i) * r + j) * 2)));
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j = 64 * jb + 4 * p + c;
-          R.v[jb][c] = buf_load16(rv, (lv && j < r) ? (uint32_t)((j * L + l) * 2) : kOffNone);
+          R.v[jb][c] = buf_load16(rv, off_if(lv && j < r, (uint32_t)((j * L + l) * 2)));
         }
       }
     }
@@ -124,13 +124,21 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
   };
 
   // Two register sets: the loads of step s+1 are in flight while step s runs.
-  Regs RA, RB;
-  load(0, RA);
-  for (int s = 0; s < nsteps; s += 2) {
-    load(s + 1, RB);
-    compute(RA);
-    load(s + 2, RA);
-    compute(RB);
+  // A ring of D register sets: the loads of step s + D - 1 are issued
+  // before step s computes, so D - 1 steps of loads are always in flight;
+  // each slot is fenced so the compiler keeps that order.  Steps past the
+  // wave's range load zeros.
+  constexpr int D = JB == 1 ? 4 : 2;
+  Regs R[D];
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k) load(k, R[k]);
+  for (int s = 0; s < nsteps; s += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load(s + k + D - 1, R[(k + D - 1) % D]);
+      compute(R[k]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // Sum the four waves' partials in wave order and store this chunk's tile.
@@ -317,11 +325,14 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
   // M viewed from this chunk's first token: masked lanes (m past C, t past
   // this wave's range) load zero through an offset past the view.
   const rsrc_t rm = make_rsrc(M + tbeg * C, (tend - tbeg) * C * 2);
+  const int wlen = (int)(wt1 - tbeg);  // tokens of this wave's range, counted from the view's first
   auto load = [&](int s, Regs& R) {
     const int64_t t = wt0 + 32 * s + 8 * g;
+    const int tl = (int)(t - tbeg);
+    const uint32_t base = (uint32_t)((tl * C + m) * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      R.a[i] = buf_load8(rm, (mv && t + i < wt1) ? (uint32_t)(((t + i - tbeg) * C + m) * 2) : kOffNone);
+      R.a[i] = buf_load8(rm, off_if(mv && tl + i < wlen, base + (uint32_t)(i * C * 2)));
     // The planes are zero for t >= T and hold TP >= T columns, so the loads
     // need no token mask; steps past this wave's range are masked via M.
 #pragma unroll
@@ -343,13 +354,18 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
     }
   };
 
-  Regs RA, RB;
-  load(0, RA);
-  for (int s = 0; s < nsteps; s += 2) {
-    load(s + 1, RB);
-    compute(RA);
-    load(s + 2, RA);
-    compute(RB);
+  // Ring of D register sets, as in the rowdot partials.
+  constexpr int D = JT == 4 ? 3 : 2;
+  Regs R[D];
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k) load(k, R[k]);
+  for (int s = 0; s < nsteps; s += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load(s + k + D - 1, R[(k + D - 1) % D]);
+      compute(R[k]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // D[j][m]: lane holds rows j = 16 jt + 4g + i, column m = m0 + 4p + c.

@@ -1,17 +1,20 @@
 // Split-contraction combine for the 256 x 256-tile dequant-GEMMs.
 //
-// A tile's contraction is cut into S slices run by S workgroups.  Every
-// slice writes its fp32 accumulators to its own slot of a workspace region,
-// then takes a ticket from the tile's counter; the workgroup that draws the
-// last ticket sums the S slots in slot order (its own from registers), so the
-// result does not depend on which slice finished last, and resets the
-// counter to zero for the next launch.  Nothing waits on another workgroup.
+// A tile's contraction is cut into S slices run by S workgroups.  A slice
+// that has finished its part draws a ticket from the tile's counter; all but
+// the last ticket write their fp32 accumulators to their own slot of a
+// workspace region and then bump the tile's published count.  The last
+// ticket waits until the other S - 1 slices have published (they drew their
+// tickets first, so they are running and need nothing from anyone to finish),
+// sums the S parts in slot order (its own from registers), so the result does
+// not depend on which slice finished last, and resets both counts to zero
+// for the next launch.  Only S - 1 slices write partials.
 //
-// The slots and the counter are accessed with system-scope cache policy
-// (stores and loads that no XCD's caches keep, atomics at the coherence
-// point), so the hand-off holds wherever the slices run, and no cache has to
-// be written back or invalidated: a device-scope fence would write back and
-// invalidate the whole L2 of the XCD, which stalls every workgroup on it.
+// Slots and counts are accessed with system-scope cache policy (stores and
+// loads that no XCD's caches keep, atomics at the coherence point), so the
+// hand-off holds wherever the slices run and no cache has to be written back
+// or invalidated: a device-scope fence would write back and invalidate the
+// whole L2 of the XCD, which stalls every workgroup on it.
 #pragma once
 
 #include "common.hpp"
@@ -23,31 +26,46 @@ constexpr int kCachePolicySystem = 1 | 16;   // sc0 | sc1
 
 // Returns true in the workgroup that must finish the tile (acc then holds the
 // full sum); false in the others, which must exit without storing.  Called by
-// all NT threads of the workgroup; flag is one int of LDS.
+// all NT threads of the workgroup; flag is one int of LDS.  `ticket` and
+// `published` are the tile's two counts (zero on entry, left zero).
 template <int NA, int NB, int NT = 256>
-__device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __restrict__ slots, int* counter,
-                                               int S, int sidx, int* flag) {
+__device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __restrict__ slots, int* ticket,
+                                               int* published, int S, int sidx, int* flag) {
   static_assert(NA * NB * 16 * NT == kSplitSlotFloats, "tile size");
   const int tid = threadIdx.x;
   const rsrc_t rs = make_rsrc(slots, (int64_t)S * kSplitSlotFloats * 4);
-  const uint32_t mine = (uint32_t)sidx * kSplitSlotFloats * 4;
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const uint32_t off = (uint32_t)((((a * NB + b) * 4 + e4) * NT + tid) * 16);
-        const u32x4 v = u32x4{__float_as_uint(acc[a][b][4 * e4]), __float_as_uint(acc[a][b][4 * e4 + 1]),
-                              __float_as_uint(acc[a][b][4 * e4 + 2]), __float_as_uint(acc[a][b][4 * e4 + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                               rs, (int)(mine + off), 0, kCachePolicySystem);
-      }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's slot stores are complete
+  __syncthreads();  // flag is free
+  if (tid == 0) *flag = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
-  if (tid == 0) *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (*flag != S - 1) {
+    const uint32_t mine = (uint32_t)sidx * kSplitSlotFloats * 4;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint32_t off = (uint32_t)((((a * NB + b) * 4 + e4) * NT + tid) * 16);
+          const u32x4 v = u32x4{__float_as_uint(acc[a][b][4 * e4]), __float_as_uint(acc[a][b][4 * e4 + 1]),
+                                __float_as_uint(acc[a][b][4 * e4 + 2]), __float_as_uint(acc[a][b][4 * e4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rs, (int)(mine + off), 0,
+              kCachePolicySystem);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's slot stores are complete
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(published, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return false;
+  }
+  // The others hold earlier tickets: they are past their main loops and
+  // only store and publish.  The bound is a guard that is never reached.
+  if (tid == 0) {
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+      if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= S - 1) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
   __syncthreads();
-  if (*flag != S - 1) return false;
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -77,7 +95,10 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
         acc[a][b][4 * e4 + 2] = sum.z;
         acc[a][b][4 * e4 + 3] = sum.w;
       }
-  if (tid == 0) __hip_atomic_exchange(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (tid == 0) {
+    __hip_atomic_exchange(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_exchange(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   return true;
 }
 
@@ -95,7 +116,7 @@ struct SplitPlan {
   int items;      // items per XCD
   int steps;      // contraction steps of a tile
   int steps_per;  // contraction steps of a slice
-  int nsplit() const { return 8 * (tx - full); }  // split tiles, including any past `tiles`
+  __host__ __device__ int nsplit() const { return 8 * (tx - full); }  // split tiles, including any past `tiles`
 };
 
 inline SplitPlan make_split_plan(int64_t tiles, int64_t steps) {
