@@ -127,8 +127,9 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
   // A ring of D register sets: the loads of step s + D - 1 are issued
   // before step s computes, so D - 1 steps of loads are always in flight;
   // each slot is fenced so the compiler keeps that order.  Steps past the
-  // wave's range load zeros.
-  constexpr int D = JB == 1 ? 4 : 2;
+  // wave's range load zeros.  (Deeper rings measured no faster: the
+  // register cost lowers occupancy.)
+  constexpr int D = 2;
   Regs R[D];
 #pragma unroll
   for (int k = 0; k < D - 1; ++k) load(k, R[k]);
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
   };
 
   // Ring of D register sets, as in the rowdot partials.
-  constexpr int D = JT == 4 ? 3 : 2;
+  constexpr int D = 2;
   Regs R[D];
 #pragma unroll
   for (int k = 0; k < D - 1; ++k) load(k, R[k]);
