@@ -42,8 +42,8 @@ GEMV = (4, 4096, 4096)
 
 # kernel -> (workload tag, sources it is built from)
 KERNEL_SOURCES = {
-    "gemm_fwd_kernel": ("mlp7b", ["gemm_fwd.hip", "gemm.hpp", "common.hpp"]),
-    "gemm_dx_kernel": ("mlp7b", ["gemm_dx.hip", "gemm.hpp", "common.hpp"]),
+    "gemm_fwd_kernel": ("mlp7b", ["gemm_fwd.hip", "gemm.hpp", "splitk.hpp", "common.hpp"]),
+    "gemm_dx_kernel": ("mlp7b", ["gemm_dx.hip", "gemm.hpp", "splitk.hpp", "common.hpp"]),
     "tokdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
     "rowdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
     "gemv_fwd_kernel": ("gemv7b", ["gemv.hip", "gemm.hpp", "common.hpp"]),
