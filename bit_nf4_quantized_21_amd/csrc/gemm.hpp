@@ -15,7 +15,9 @@ struct FwdGemmParams {
   const uint8_t* q8;     // [N*K/64]
   const float* s2;       // [ceil(N*K/64/256)]
   const uint16_t* B;     // [r,N] bf16
-  const float* XA;       // [T,r] fp32 (GEMV path)
+  float* XA;             // [T,r] fp32 out (GEMV path: written by the GEMV from P)
+  const float* P;        // GEMV path: the rowdot's chunk partials of XA, [nc][T][RP]
+  int nc;                // their chunk count (<= 8)
   const uint16_t* XAh;   // [T,RP] bf16 hi part of s*XA, zero past r (GEMM path)
   const uint16_t* XAl;   // [T,RP] bf16 lo part
   uint16_t* Y;           // [T,N] bf16

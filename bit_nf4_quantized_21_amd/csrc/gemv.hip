@@ -56,32 +56,40 @@ __global__ __launch_bounds__(512) void gemv_fwd_kernel(FwdGemmParams p, Codebook
   const rsrc_t rq = make_rsrc(p.q8, N * bpr);
   const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
   const rsrc_t rx = make_rsrc(p.X, T * K * 2);
+  // A chunk past the last one loads nothing at all: its offsets are pushed
+  // past every view (no memory traffic, no branch).
   auto load = [&](int64_t c, ChunkRegs& R) {
     const int64_t k0 = c * 128 + 32 * g;
+    const bool cv = c < nchunk;
     const bool kv = k0 < K;  // K % 64 == 0: a 32-k group is whole or absent
-    R.c = buf_load16(rc, (uint32_t)(n * K2 + k0 / 2));
+    R.c = buf_load16(rc, off_if(cv, (uint32_t)(n * K2 + k0 / 2)));
     const int64_t b = n * bpr + k0 / 64;
-    R.q = buf_load1(rq, (uint32_t)b);
-    R.s2 = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
-    const uint32_t xo = kv ? (uint32_t)(((int64_t)l16 * K + k0) * 2) : 0x7FFFFF00u;
+    R.q = buf_load1(rq, off_if(cv, (uint32_t)b));
+    R.s2 = __uint_as_float(buf_load4(rs, off_if(cv, (uint32_t)((b >> 8) * 4))));
+    const uint32_t xo = off_if(kv, (uint32_t)(((int64_t)l16 * K + k0) * 2));
 #pragma unroll
     for (int s = 0; s < 4; ++s) R.x[s] = buf_load16(rx, xo + 16 * s);
   };
 
-  // The adapter operands (XA, T*r <= 2048 floats, and the workgroup's r x 16
-  // slice of B) are requested first from clamped, in-bounds addresses, then
-  // the first four weight chunks of every wave; the adapter values are stored
-  // to LDS once they arrive, which waits for nothing issued after them.
-  const int nx = (int)T * r, nbv = r * kRowsPerWG;
-  float xv[4];
+  // The adapter operands are requested first: the rowdot's chunk partials of
+  // XA (T*RP <= 2048 values, at most 8 chunks each; value v = tid + 512q)
+  // and the workgroup's r x 16 slice of B, from clamped in-bounds addresses
+  // or zero-returning offsets; then the first four weight chunks of every
+  // wave.  The adapter values are summed and stored to LDS once they arrive,
+  // which waits for nothing issued after them.
+  const int RPv = p.RP, nv = (int)T * RPv, nbv = r * kRowsPerWG;
+  const rsrc_t rp = make_rsrc(p.P, (int64_t)p.nc * nv * 4);
+  float xpart[4][8];
   uint16_t bv[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = tid + 512 * k;
-    xv[k] = p.XA[i < nx ? i : nx - 1];
-    const int ib = i < nbv ? i : nbv - 1;
+  for (int q = 0; q < 4; ++q) {
+    const int v = tid + 512 * q;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      xpart[q][c] = __uint_as_float(buf_load4(rp, off_if(v < nv && c < p.nc, (uint32_t)((c * nv + v) * 4))));
+    const int ib = v < nbv ? v : nbv - 1;
     const int64_t nn = n0 + ib % kRowsPerWG;
-    bv[k] = p.B[(int64_t)(ib / kRowsPerWG) * N + (nn < N ? nn : N - 1)];
+    bv[q] = p.B[(int64_t)(ib / kRowsPerWG) * N + (nn < N ? nn : N - 1)];
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   ChunkRegs R[4] = {};
@@ -90,11 +98,21 @@ __global__ __launch_bounds__(512) void gemv_fwd_kernel(FwdGemmParams p, Codebook
   for (int i = 0; i < 4; ++i) load(c0 + i * kWaves, R[i]);
 
   codebook_to_lds(lut, cb, tid);
+  // XA = the chunk partials summed in chunk order; workgroup 0 also returns it.
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = tid + 512 * k;
-    if (i < nx) xa_s[i / r][i % r] = xv[k];
-    if (i < nbv) b_s[i / kRowsPerWG][i % kRowsPerWG] = n0 + i % kRowsPerWG < N ? bf16_to_f32(bv[k]) : 0.0f;
+  for (int q = 0; q < 4; ++q) {
+    const int v = tid + 512 * q;
+    float x = xpart[q][0];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) x += xpart[q][c];  // chunks past nc read zero
+    if (v < nv) {
+      const int t = v / RPv, j = v % RPv;
+      if (j < r) {
+        xa_s[t][j] = x;
+        if (blockIdx.x == 0) p.XA[t * r + j] = x;
+      }
+    }
+    if (v < nbv) b_s[v / kRowsPerWG][v % kRowsPerWG] = n0 + v % kRowsPerWG < N ? bf16_to_f32(bv[q]) : 0.0f;
   }
   __syncthreads();
 

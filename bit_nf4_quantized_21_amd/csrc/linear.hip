@@ -41,6 +41,16 @@ int64_t row_chunk(int64_t T, int64_t L) {
   return round_up(cdiv(L, nc), 128);
 }
 
+// Chunk of the X A rowdot on the GEMV path (T <= 16): at most 8 chunks, so
+// the GEMV can sum the partials it needs (T * RP values, 8 chunks each) with
+// all their loads in flight at once.
+int64_t gemv_row_chunk(int64_t K) {
+  int64_t nc = cdiv(K, 128);
+  if (nc > 8) nc = 8;
+  return round_up(cdiv(K, nc), 128);
+}
+int64_t fwd_row_chunk(int64_t T, int64_t K) { return T <= kGemvMaxT ? gemv_row_chunk(K) : row_chunk(T, K); }
+
 // Token chunk of a tokdot (X^T G or dY^T XA): about 256 workgroups of 64
 // columns each, chunks a multiple of 128 tokens.
 int64_t tok_chunk(int64_t T, int64_t C) {
@@ -81,7 +91,7 @@ struct FwdLayout {
 };
 FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   FwdLayout l{};
-  l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
+  l.p = align256((size_t)cdiv(K, fwd_row_chunk(T, K)) * T * rpad(r) * sizeof(float));
   if (T > kGemvMaxT) {
     l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
     l.g = fwd_plan(T, K, N);
@@ -109,7 +119,7 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   char* w = reinterpret_cast<char*>(ws);
   float* P = reinterpret_cast<float*>(w);
   RowdotOut o{};
-  o.f32 = XA;
+  if (a.T > kGemvMaxT) o.f32 = XA;  // the GEMV path sums the partials itself
   uint16_t* XAh = reinterpret_cast<uint16_t*>(w + l.p);
   uint16_t* XAl = reinterpret_cast<uint16_t*>(w + l.p + l.xah);
   char* w2 = w + l.p + 2 * l.xah;
@@ -120,7 +130,8 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
     o.zero = reinterpret_cast<int*>(w2 + l.slots);  // the GEMM's split tickets
     o.nzero = 2 * l.g.nsplit();
   }
-  hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
+  const int64_t LC = fwd_row_chunk(a.T, a.K);
+  hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, LC, s);
   if (e != hipSuccess) return e;
   FwdGemmParams p{};
   p.X = X;
@@ -129,6 +140,8 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   p.s2 = a.s2;
   p.B = a.B;
   p.XA = XA;
+  p.P = P;
+  p.nc = (int)cdiv(a.K, LC);
   p.Y = Y;
   p.T = a.T;
   p.K = a.K;
