@@ -132,6 +132,9 @@ __device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
@@ -212,6 +215,28 @@ __device__ __forceinline__ uint32_t byte_x8(uint32_t x, int q) {
 // the table visible with a barrier.
 __device__ __forceinline__ void pair_table_to_lds(unsigned char* lds, const float* lut16, int tid) {
   if (tid < 256) reinterpret_cast<float2*>(lds)[tid] = make_float2(lut16[tid & 15], lut16[tid >> 4]);
+}
+// The same table built from the kernel argument by lane selects.  The
+// values pass through an empty asm first, so the selects cannot be folded
+// into a lane-indexed read of the argument (a memory load that would wait
+// for every load issued before it).
+__device__ __forceinline__ void pair_table_from_arg(unsigned char* lds, const Codebook& cb, int tid) {
+  if (tid < 256) {
+    float c[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      c[e] = cb.c[e];
+      asm volatile("" : "+v"(c[e]));
+    }
+    const uint32_t lo = tid & 15, hi = tid >> 4;
+    float a = c[0], b = c[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+      a = lo == (uint32_t)e ? c[e] : a;
+      b = hi == (uint32_t)e ? c[e] : b;
+    }
+    reinterpret_cast<float2*>(lds)[tid] = make_float2(a, b);
+  }
 }
 // Codebook values of the 8 codes of a dword from the pair table.
 __device__ __forceinline__ void lut8_pairs(const unsigned char* lds, uint32_t x, float (&f)[8]) {

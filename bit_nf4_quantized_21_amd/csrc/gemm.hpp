@@ -15,9 +15,10 @@ struct FwdGemmParams {
   const uint8_t* q8;     // [N*K/64]
   const float* s2;       // [ceil(N*K/64/256)]
   const uint16_t* B;     // [r,N] bf16
-  float* XA;             // [T,r] fp32 out (GEMV path: written by the GEMV from P)
-  const float* P;        // GEMV path: the rowdot's chunk partials of XA, [nc][T][RP]
-  int nc;                // their chunk count (<= 8)
+  float* XA;             // [T,r] fp32 out (GEMV path: computed by the GEMV itself)
+  const uint16_t* A;     // [K,r] bf16 (GEMV path)
+  float* P;              // GEMV path: partials of XA, [nparts][T][RP]
+  int nparts;            // GEMV path: their count (filled by the launcher)
   const uint16_t* XAh;   // [T,RP] bf16 hi part of s*XA, zero past r (GEMM path)
   const uint16_t* XAl;   // [T,RP] bf16 lo part
   uint16_t* Y;           // [T,N] bf16
@@ -46,6 +47,13 @@ struct DxGemmParams {
   SplitPlan plan;        // filled by the launcher
   int tiles_k, tiles_t;
 };
+
+// Grid of the GEMV and the slices of its XA partials: partial b < nparts
+// sums the contraction over [b ks, min(K, (b+1) ks)).
+struct GemvPlan {
+  int grid, nparts, ks;
+};
+GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r);
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);
 hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);

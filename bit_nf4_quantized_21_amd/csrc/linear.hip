@@ -1,10 +1,12 @@
 // Orchestration of the forward and backward passes of the frozen NF4 linear
 // layer with a LoRA adapter: workspace layout, path choice and launch order.
 //
-// Forward  (Y = X W'^T + s (X A) B, XA = X A):
-//   1. rowdot X A  -> chunk partials -> XA (fp32, also the caller's output)
-//   2. T <= 16: dequant-GEMV;  T > 16: dequant-GEMM; both add s XA B in
-//      their epilogue.
+// Forward  (Y = X W'^T + s (X A) B, XA = X A; XA is also the caller's output):
+//   T <= 16: 1. XA partials over slices of K (MFMA)
+//            2. dequant-GEMV, summing the partials into XA and adding s XA B
+//               in its epilogue.
+//   T > 16:  1. rowdot X A -> chunk partials -> XA
+//            2. dequant-GEMM, adding s XA B in its epilogue.
 // Backward (G = dY B^T; dX = dY W' + s G A^T; dA = s X^T G; dB = s XA^T dY):
 //   1. rowdot dY B^T -> G, kept as bf16 hi / lo parts: rows of s G for the
 //      dX GEMM, transposed planes of G and of XA for the two tokdots
@@ -41,16 +43,6 @@ int64_t row_chunk(int64_t T, int64_t L) {
   return round_up(cdiv(L, nc), 128);
 }
 
-// Chunk of the X A rowdot on the GEMV path (T <= 16): at most 8 chunks, so
-// the GEMV can sum the partials it needs (T * RP values, 8 chunks each) with
-// all their loads in flight at once.
-int64_t gemv_row_chunk(int64_t K) {
-  int64_t nc = cdiv(K, 128);
-  if (nc > 8) nc = 8;
-  return round_up(cdiv(K, nc), 128);
-}
-int64_t fwd_row_chunk(int64_t T, int64_t K) { return T <= kGemvMaxT ? gemv_row_chunk(K) : row_chunk(T, K); }
-
 // Token chunk of a tokdot (X^T G or dY^T XA): about 256 workgroups of 64
 // columns each, chunks a multiple of 128 tokens.
 int64_t tok_chunk(int64_t T, int64_t C) {
@@ -83,16 +75,18 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
 }
 }  // namespace
 
-// Forward workspace: rowdot partials, then (GEMM path) split partials and
-// tile counters.
+// Forward workspace: GEMV path, the XA partials; GEMM path,
+// rowdot partials, bf16 parts of s XA, split partials and tile counters.
 struct FwdLayout {
   size_t p, xah, slots, counters, total;
   SplitPlan g;
 };
 FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   FwdLayout l{};
-  l.p = align256((size_t)cdiv(K, fwd_row_chunk(T, K)) * T * rpad(r) * sizeof(float));
-  if (T > kGemvMaxT) {
+  if (T <= kGemvMaxT) {
+    l.p = align256((size_t)gemv_plan(N, K, T, r).nparts * T * rpad(r) * sizeof(float));
+  } else {
+    l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
     l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
     l.g = fwd_plan(T, K, N);
     l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
@@ -118,30 +112,29 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   const FwdLayout l = fwd_layout(a.T, a.K, a.N, a.r);
   char* w = reinterpret_cast<char*>(ws);
   float* P = reinterpret_cast<float*>(w);
-  RowdotOut o{};
-  if (a.T > kGemvMaxT) o.f32 = XA;  // the GEMV path sums the partials itself
   uint16_t* XAh = reinterpret_cast<uint16_t*>(w + l.p);
   uint16_t* XAl = reinterpret_cast<uint16_t*>(w + l.p + l.xah);
   char* w2 = w + l.p + 2 * l.xah;
   if (a.T > kGemvMaxT) {
+    RowdotOut o{};
+    o.f32 = XA;
     o.row_hi = XAh;  // s XA as bf16 hi / lo rows for the GEMM's adapter steps
     o.row_lo = XAl;
     o.scale_row = a.s;
     o.zero = reinterpret_cast<int*>(w2 + l.slots);  // the GEMM's split tickets
     o.nzero = 2 * l.g.nsplit();
+    hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
+    if (e != hipSuccess) return e;
   }
-  const int64_t LC = fwd_row_chunk(a.T, a.K);
-  hipError_t e = launch_rowdot(X, a.A, /*v_lr=*/true, P, o, a.T, a.K, a.r, LC, s);
-  if (e != hipSuccess) return e;
   FwdGemmParams p{};
   p.X = X;
   p.codes = a.codes;
   p.q8 = a.q8;
   p.s2 = a.s2;
+  p.A = a.A;
   p.B = a.B;
   p.XA = XA;
   p.P = P;
-  p.nc = (int)cdiv(a.K, LC);
   p.Y = Y;
   p.T = a.T;
   p.K = a.K;

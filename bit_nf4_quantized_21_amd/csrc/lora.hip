@@ -256,35 +256,6 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
   }
 }
 
-// Few-token rowdot reduction (fp32 result only): 16 float4 outputs per
-// workgroup, 16 threads per output each summing every 16th chunk in chunk
-// order, then the 16 sums added in thread order, so all loads of a thread
-// are in flight together and the order is fixed.
-__global__ __launch_bounds__(256) void rowdot_reduce_small_kernel(float* __restrict__ out,
-                                                                  const float* __restrict__ P, int64_t T, int r,
-                                                                  int RP, int nc) {
-  __shared__ float4 part[16][17];
-  const int o = threadIdx.x & 15, cg = threadIdx.x >> 4;
-  const int64_t q = (int64_t)blockIdx.x * 16 + o;  // float4 index into [T][RP]
-  const int64_t t = q / (RP / 4);
-  const int j = (int)(q % (RP / 4)) * 4;
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < T) {
-    for (int c = cg; c < nc; c += 16) {
-      const float4 x = *reinterpret_cast<const float4*>(P + ((int64_t)c * T + t) * RP + j);
-      v = c == cg ? x : add4(v, x);
-    }
-  }
-  part[o][cg] = v;
-  __syncthreads();
-  if (cg == 0 && t < T && j < r) {
-    float4 sum = part[o][0];
-#pragma unroll
-    for (int g = 1; g < 16; ++g) sum = add4(sum, part[o][g]);
-    *reinterpret_cast<float4*>(out + t * r + j) = sum;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // tokdot partials.  Workgroup = 4 waves = 64 columns m x one chunk of t;
 // wave w takes the w-th quarter of the chunk, 32 t per step.  MFMA
@@ -467,14 +438,6 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float*
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!o.f32 && !o.row_hi && !o.t_hi && !o.side && o.nzero == 0) return hipSuccess;  // partials for a consumer
-  const bool f32_only = !o.row_hi && !o.t_hi && !o.side && o.nzero == 0;
-  if (T <= 16 && f32_only) {
-    KernelTimer kt_("rowdot_reduce_kernel", s);
-    hipLaunchKernelGGL(rowdot_reduce_small_kernel, dim3((unsigned)cdiv(T * 16 * JB, 16)), dim3(256), 0, s, o.f32, P, T,
-                       r, 64 * JB, (int)nc);
-    return hipGetLastError();
-  }
   {
     KernelTimer kt_("rowdot_reduce_kernel", s);
     hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)(cdiv(T, 64) * (64 / kRedRows)), (unsigned)JB), dim3(256),

@@ -24,9 +24,7 @@ struct RowdotOut {
 };
 
 // out[T][r] = M[T,L] V  with V = A[L,r] (v_lr) or B[r,L]^T.  P is scratch of
-// ceil(L/LC) * T * RP floats; LC a multiple of 128.  With every output of `o`
-// null, only the chunk partials are written, P[c][t][j] (row stride RP), for
-// a later kernel to sum.
+// ceil(L/LC) * T * RP floats; LC a multiple of 128.
 hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
                          int64_t L, int r, int64_t LC, hipStream_t s);
 

@@ -98,6 +98,43 @@ def test_gemv_path_small_tokens(T):
     _check(c, c.gpu())
 
 
+@pytest.mark.parametrize("N,K,T,r", [(1000, 11008, 3, 128), (24, 64, 16, 8), (4104, 2048, 9, 72),
+                                     (776, 8192, 2, 64)])
+def test_gemv_path_ragged(N, K, T, r):
+    """GEMV path with N not a multiple of 16, one to 32 XA producers (last
+    slice short), adapter ranks 8, 64, 72 and 128."""
+    print(f"gemv ragged N={N} K={K} T={T} r={r}", flush=True)
+    c = Case(N, K, T, r, seed=N + K + T + r)
+    _check(c, c.gpu(bwd=False), bwd=False)
+
+
+def test_gemv_path_repeated_calls_identical():
+    """More back-to-back GEMV-path calls than there are hand-off records, two
+    shapes interleaved: every call returns exactly the first call's result."""
+    print("gemv repeat", flush=True)
+    q = _q()
+    outs = []
+    for (N, K, T, r, seed) in [(512, 1024, 4, 16, 21), (272, 4096, 7, 128, 22)]:
+        c = Case(N, K, T, r, seed=seed)
+        Wg = torch.from_numpy(c.W.ravel()).cuda()
+        codes, absmax = q.quantize_nf4(Wg)
+        q8, s2 = q.double_quant(absmax)
+        outs.append((c, codes, q8, s2, _bf16_dev(c.Xb), _bf16_dev(c.Ab), _bf16_dev(c.Bb)))
+    first = []
+    for (c, codes, q8, s2, Xg, Ag, Bg) in outs:
+        first.append(q.linear_fwd(Xg, codes, q8, s2, Ag, Bg, c.alpha, c.N))
+    torch.cuda.synchronize()
+    for it in range(150):
+        i = it % 2
+        c, codes, q8, s2, Xg, Ag, Bg = outs[i]
+        Y, XA = q.linear_fwd(Xg, codes, q8, s2, Ag, Bg, c.alpha, c.N)
+        assert torch.equal(Y, first[i][0]) and torch.equal(XA, first[i][1]), it
+    c = outs[1][0]
+    Wd = c.oracle_weight()[3]
+    Yref, _ = lora.linear_fwd(c.X, Wd, c.A, c.B, c.alpha, c.r)
+    _assert_close("Y", _f32(first[1][0]), Yref)
+
+
 def test_tiny_config_fwd_bwd():
     """W 512x512, X 32x512, r=8, alpha=16: the small workload in full."""
     print("tiny", flush=True)
