@@ -22,11 +22,13 @@
 //    X operands of substep s+1 are read from LDS and chunk s of the next
 //    step's W is looked up, scaled and packed to bf16, each MFMA carrying a
 //    fixed share of that work (a substep is 16 fenced slices).  X tiles go
-//    through a 3-stage LDS ring: each lane loads its 8 x 16 bytes of the
-//    tile two steps ahead into registers and writes them to LDS one step
-//    later, so every global load has a full step to arrive before anything
-//    waits on it.  Codes are loaded two steps ahead into registers.  One
-//    barrier per step sits after substep 2, so the next step's first
+//    through a 4-stage LDS ring filled by buffer-to-LDS loads issued two
+//    steps ahead (no registers, no LDS write instructions); each stage is
+//    its own LDS object, so the compiler can tell the stage being filled
+//    from the ones being read and puts no wait before the reads.  Codes are
+//    loaded two steps ahead into registers.  One barrier per step, before
+//    substep 3, waits only for the loads the next step reads (an explicit
+//    count leaves the younger ones in flight), so the next step's first
 //    operand reads overlap substep 3.
 //  * X rows are 128 bytes in LDS with the 16-byte chunk index XOR-ed with
 //    bits 1..3 of the row: the 16 rows read by one 16-lane phase land in 16
