@@ -240,11 +240,13 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
   }
   if (!want_t && !want_side) return;  // uniform per workgroup
   __syncthreads();
-  // Transposed planes: thread q < 128 writes 8 consecutive t of row j.
+  // Tokdot planes: thread q < 128 writes 8 consecutive t of row j, one
+  // 16-byte unit of the blocked order.
   if (threadIdx.x < 64 * kRedRows / 8) {
     const int q = threadIdx.x;
     const int j = q / (kRedRows / 8), t8 = 8 * (q % (kRedRows / 8));
-    const int64_t off = (int64_t)(64 * jb + j) * o.TP + t0 + t8;
+    const int64_t jj = 64 * jb + j, tt = t0 + t8;
+    const int64_t off = (((tt >> 5) * (RP / 16) + (jj >> 4)) * 64 + (jj & 15) + 16 * ((tt & 31) >> 3)) * 8;
     if (want_t) {
       *reinterpret_cast<u32x4*>(o.t_hi + off) = *reinterpret_cast<const u32x4*>(&tr[0][j * kPad + t8]);
       *reinterpret_cast<u32x4*>(o.t_lo + off) = *reinterpret_cast<const u32x4*>(&tr[1][j * kPad + t8]);
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
 // ---------------------------------------------------------------------------
 // tokdot partials.  Workgroup = 4 waves = 64 columns m x one chunk of t;
 // wave w takes the w-th quarter of the chunk, 32 t per step.  MFMA
-// orientation D[j][m]: A operand = S^T from the transposed hi / lo planes
+// orientation D[j][m]: A operand = S^T from the hi / lo tokdot planes
 // (row j = 16 jt + p, 8 consecutive t), B operand = M transposed in
 // registers (8 consecutive t of column m = m0 + 4p + c).
 // P[c][j][m] has RP rows per chunk.
@@ -305,11 +307,13 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       R.a[i] = buf_load8(rm, off_if(mv && tl + i < wlen, base + (uint32_t)(i * C * 2)));
-    // The planes are zero for t >= T and hold TP >= T columns, so the loads
-    // need no token mask; steps past this wave's range are masked via M.
+    // The planes are zero for t >= T and hold TP >= T tokens, so the loads
+    // need no token mask; steps past this wave's range (masked via M) read
+    // the chunk's first block.  Each load is 1 KB of consecutive bytes.
+    const int64_t blk = (t < tend ? t : tbeg) >> 5;
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
-      const int64_t off = (int64_t)(16 * jt + p) * TP + (t < tend ? t : tbeg);
+      const int64_t off = ((blk * JT + jt) * 64 + lane) * 8;
       R.h[jt] = *reinterpret_cast<const u32x4*>(Sh + off);
       R.l[jt] = *reinterpret_cast<const u32x4*>(Sl + off);
     }

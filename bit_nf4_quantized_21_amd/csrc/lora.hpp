@@ -8,16 +8,22 @@ namespace qlora {
 
 // Outputs of a rowdot reduction (each optional: null skips it).  RP is r
 // rounded up to 64; TP is T rounded up to 64.
+//
+// A "tokdot plane" holds an RP x TP bf16 matrix S^T (element (j, t)) in the
+// order the tokdot's MFMAs read it: 16-byte unit
+//   u = ((t / 32) * (RP / 16) + j / 16) * 64 + (j % 16) + 16 * ((t % 32) / 8)
+// holds t % 8 = 0..7, so one wave's A operand for 32 tokens and 16 rows j is
+// 1 KB of consecutive bytes.  Zero outside T x r.
 struct RowdotOut {
   float* f32;            // [T][r] fp32 result
   uint16_t* row_hi;      // [T][RP] bf16 hi part of scale_row * result
   uint16_t* row_lo;      // [T][RP] bf16 lo part
   float scale_row;
-  uint16_t* t_hi;        // [RP][TP] bf16 hi part of the result, transposed
-  uint16_t* t_lo;        // [RP][TP] bf16 lo part
+  uint16_t* t_hi;        // tokdot plane: bf16 hi part of the result
+  uint16_t* t_lo;        // tokdot plane: bf16 lo part
   int64_t TP;
-  const float* side;     // optional extra [T][r] fp32 input, transposed and split
-  uint16_t* side_hi;     // into [RP][TP] hi / lo planes
+  const float* side;     // optional extra [T][r] fp32 input, split into
+  uint16_t* side_hi;     // hi / lo tokdot planes
   uint16_t* side_lo;
   int* zero;             // optional ints set to zero (counters of a later kernel)
   int64_t nzero;
@@ -29,7 +35,7 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float*
                          int64_t L, int r, int64_t LC, hipStream_t s);
 
 // out = bf16(scale * M[T,C]^T S[T,r]) stored [r,C] (or [C,r] when m_major),
-// with S given as transposed hi / lo planes [RP][TP].  P is scratch of
+// with S given as hi / lo tokdot planes (RowdotOut).  P is scratch of
 // ceil(T/TC) * RP * C floats; TC a multiple of 128.
 hipError_t launch_tokdot(const uint16_t* M, const uint16_t* Sh, const uint16_t* Sl, int64_t TP, float* P,
                          uint16_t* out, int64_t T, int64_t C, int r, int64_t TC, float scale, bool m_major,

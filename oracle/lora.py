@@ -72,3 +72,18 @@ def dx_rows(dY_rows, Wd, A, B, alpha: float, r: int):
     s = lora_scale(alpha, r)
     G = dY_rows @ np.asarray(B, dtype=np.float64).T
     return dY_rows @ np.asarray(Wd, dtype=np.float64) + s * (G @ np.asarray(A, dtype=np.float64).T)
+
+
+def adapter_grads(dY, X, A, B, alpha: float, r: int):
+    """R8 for the adapter alone: (dA [K,r], dB [r,N], G [T,r]) in fp64, the
+    same products as linear_bwd without dX (which needs the whole base
+    weight)."""
+    dY = np.asarray(dY, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    s = lora_scale(alpha, r)
+    G = dY @ B.T
+    dA = s * (X.T @ G)
+    dB = s * ((X @ A).T @ dY)
+    return dA, dB, G

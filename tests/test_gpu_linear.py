@@ -86,7 +86,7 @@ def _check(case, out, rows=None, bwd=True):
         return
     dXref = lora.dx_rows(case.dY[rows], Wd, case.A, case.B, case.alpha, case.r)
     _assert_close("dX", _f32(out["dX"])[rows], dXref)
-    _, dAref, dBref, _ = lora.linear_bwd(case.dY, case.X, Wd, case.A, case.B, case.alpha, case.r)
+    dAref, dBref, _ = lora.adapter_grads(case.dY, case.X, case.A, case.B, case.alpha, case.r)
     _assert_close("dA", _f32(out["dA"]), dAref)
     _assert_close("dB", _f32(out["dB"]), dBref)
 
@@ -167,6 +167,19 @@ def test_llama7b_mlp_full_size_sampled(N, K):
     out = c.gpu()
     rows = np.random.Generator(np.random.PCG64(7)).choice(2048, 48, replace=False)
     rows = np.sort(np.concatenate([rows, [0, 2047]]))
+    _check(c, out, rows=rows)
+
+
+@pytest.mark.parametrize("N,K,T", [(6656, 6656, 4096), (17920, 6656, 4096), (6656, 17920, 4096),
+                                   (8192, 8192, 512), (22016, 8192, 512), (8192, 22016, 512)])
+def test_33b_65b_linears_full_size_sampled(N, K, T):
+    """The 33B layer's linears at T=4096 and the 65B set's at T=512 (r=64,
+    alpha=16): Y and dX on 40 sampled rows, dA and dB in full."""
+    print(f"full size N={N} K={K} T={T}", flush=True)
+    c = Case(N, K, T, 64, seed=N + 3 * K + T)
+    out = c.gpu()
+    rows = np.random.Generator(np.random.PCG64(11)).choice(T, 38, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, T - 1]]))
     _check(c, out, rows=rows)
 
 

@@ -71,6 +71,19 @@ def test_backward_matches_loops():
     assert np.allclose(dB, ldB, rtol=1e-12, atol=1e-13)
 
 
+def test_adapter_grads_match_loops():
+    """adapter_grads (the dA, dB used at full layer sizes) against the triple
+    loops, including the intermediate G = dY B^T."""
+    X, Wd, A, B, dY = _tiny(4, T=5, K=64, N=6, r=3)
+    s = lora.lora_scale(16.0, 3)
+    dA, dB, G = lora.adapter_grads(dY, X, A, B, 16.0, 3)
+    _, ldA, ldB = _loops_bwd(dY, X, Wd, A, B, s)
+    lG = np.array([[sum(dY[t, n] * B[j, n] for n in range(6)) for j in range(3)] for t in range(5)])
+    assert np.allclose(dA, ldA, rtol=1e-12, atol=1e-13)
+    assert np.allclose(dB, ldB, rtol=1e-12, atol=1e-13)
+    assert np.allclose(G, lG, rtol=1e-12, atol=1e-13)
+
+
 def test_gradients_by_central_differences():
     """L = <dY, Y> is linear in X, in A and in B separately, so a central
     difference along any direction equals the gradient's inner product with
