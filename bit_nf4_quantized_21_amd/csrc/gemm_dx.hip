@@ -34,8 +34,10 @@
 //    interleaved; q8 / s2 are fetched a step before their scale is stored.
 //  * The adapter term is two more steps: A (rows k) against the bf16 hi and
 //    lo planes of s G (rows t), staged into the same buffers.
-//  * Workgroup order is XCD-aware (each XCD takes a contiguous run of
-//    k-tile-major tiles, sharing the code columns of one k range).
+//  * Workgroup order is XCD-aware: each XCD takes a contiguous run of
+//    token-tile-major tiles, so the dY rows of a token tile are fetched into
+//    that XCD's L2 once and re-read there by every k-tile (measured faster
+//    than k-tile-major, which shares the code columns instead).
 #include "common.hpp"
 #include "timing.hpp"
 #include "gemm.hpp"
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
   // Workgroup-uniform values kept in scalar registers (the buffer views
   // built from them must be uniform).
-  const int tk = __builtin_amdgcn_readfirstlane(tile / p.tiles_t);
-  const int tt = __builtin_amdgcn_readfirstlane(tile % p.tiles_t);
+  const int tk = __builtin_amdgcn_readfirstlane(tile % p.tiles_k);
+  const int tt = __builtin_amdgcn_readfirstlane(tile / p.tiles_k);
   const float* const lut16 = reinterpret_cast<const float*>(smem + 2048);
   codebook_to_lds(reinterpret_cast<float*>(smem + 2048), cb, tid);
 

@@ -282,7 +282,7 @@ GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r) {
   GemvPlan g{};
   g.grid = (int)((N + kRowsPerWG - 1) / kRowsPerWG);
   const int64_t RP = (r + 63) / 64 * 64;
-  int64_t np = (K + 511) / 512;  // slices of at least 512 k
+  int64_t np = (K + 127) / 128;  // slices of at least 128 k
   const int64_t nq = (T * RP + kThreads - 1) / kThreads;
   const int64_t cap = kPartRegs / (nq <= 1 ? 1 : nq <= 2 ? 2 : 4);
   if (np > cap) np = cap;
