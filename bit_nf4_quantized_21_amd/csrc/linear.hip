@@ -9,10 +9,9 @@
 //            2. dequant-GEMM, adding s XA B in its epilogue.
 // Backward (G = dY B^T; dX = dY W' + s G A^T; dA = s X^T G; dB = s XA^T dY):
 //   1. rowdot dY B^T -> G, kept as bf16 hi / lo parts: rows of s G for the
-//      dX GEMM, transposed planes of G and of XA for the two tokdots
-//   2. tokdot dY^T XA -> dB
+//      dX GEMM, tokdot planes of G and of XA
+//   2. tokdots dY^T XA -> dB and X^T G -> dA, one launch
 //   3. dequant-GEMM dX with the s G A^T term in its epilogue
-//   4. tokdot X^T G -> dA
 // Every reduction is split into chunks whose partials are summed in a fixed
 // order, so results are bitwise reproducible.
 #include "common.hpp"
@@ -56,7 +55,7 @@ int64_t tok_chunk(int64_t T, int64_t C) {
 
 // Backward workspace regions, each 256-byte aligned.
 struct BwdLayout {
-  size_t pg, g, planes, ptok, slots, counters, total;
+  size_t pg, g, planes, ptok_b, ptok_a, slots, counters, total;
 };
 BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   BwdLayout l{};
@@ -66,11 +65,12 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   l.planes = align256((size_t)RP * TP * sizeof(uint16_t));
   const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * RP * N * sizeof(float);
   const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * RP * K * sizeof(float);
-  l.ptok = align256(pdb > pda ? pdb : pda);
+  l.ptok_b = align256(pdb);
+  l.ptok_a = align256(pda);
   const SplitPlan dp = dx_plan(T, K, N);
   l.slots = dp.S > 1 ? align256((size_t)dp.nsplit() * dp.S * kSplitSlotFloats * sizeof(float)) : 0;
   l.counters = align256((size_t)(dp.nsplit() > 0 ? 2 * dp.nsplit() : 1) * sizeof(int));
-  l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok + l.slots + l.counters;
+  l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok_b + l.ptok_a + l.slots + l.counters;
   return l;
 }
 }  // namespace
@@ -166,9 +166,11 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   uint16_t* Gtl = reinterpret_cast<uint16_t*>(w2 + l.planes);
   uint16_t* XAth = reinterpret_cast<uint16_t*>(w2 + 2 * l.planes);
   uint16_t* XAtl = reinterpret_cast<uint16_t*>(w2 + 3 * l.planes);
-  float* Ptok = reinterpret_cast<float*>(w2 + 4 * l.planes);
-  float* slots = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok);
-  int* counters = reinterpret_cast<int*>(w2 + 4 * l.planes + l.ptok + l.slots);
+  float* Ptok_b = reinterpret_cast<float*>(w2 + 4 * l.planes);
+  float* Ptok_a = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok_b);
+  char* w3 = w2 + 4 * l.planes + l.ptok_b + l.ptok_a;
+  float* slots = reinterpret_cast<float*>(w3);
+  int* counters = reinterpret_cast<int*>(w3 + l.slots);
   const SplitPlan dp = dx_plan(a.T, a.K, a.N);
   const int64_t TP = round_up(a.T, 64);
 
@@ -188,7 +190,27 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   o.nzero = 2 * dp.nsplit();
   hipError_t e = launch_rowdot(dY, a.B, /*v_lr=*/false, Pg, o, a.T, a.N, a.r, row_chunk(a.T, a.N), s);
   if (e != hipSuccess) return e;
-  e = launch_tokdot(dY, XAth, XAtl, TP, Ptok, dB, a.T, a.N, a.r, tok_chunk(a.T, a.N), a.s, /*m_major=*/false, s);
+  // dB = s XA^T dY (stored [r,N]) and dA = s X^T G (stored [K,r]) in one launch.
+  TokJob jb{}, ja{};
+  jb.M = dY;
+  jb.Sh = XAth;
+  jb.Sl = XAtl;
+  jb.P = Ptok_b;
+  jb.out = dB;
+  jb.C = a.N;
+  jb.TC = tok_chunk(a.T, a.N);
+  jb.scale = a.s;
+  jb.m_major = 0;
+  ja.M = X;
+  ja.Sh = Gth;
+  ja.Sl = Gtl;
+  ja.P = Ptok_a;
+  ja.out = dA;
+  ja.C = a.K;
+  ja.TC = tok_chunk(a.T, a.K);
+  ja.scale = a.s;
+  ja.m_major = 1;
+  e = launch_tokdot2(jb, ja, a.T, TP, a.r, s);
   if (e != hipSuccess) return e;
   DxGemmParams p{};
   p.dY = dY;
@@ -206,9 +228,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   p.RP = (int)rpad(a.r);
   p.slots = slots;
   p.counters = counters;
-  e = launch_gemm_dx(p, cb, s);
-  if (e != hipSuccess) return e;
-  return launch_tokdot(X, Gth, Gtl, TP, Ptok, dA, a.T, a.K, a.r, tok_chunk(a.T, a.K), a.s, /*m_major=*/true, s);
+  return launch_gemm_dx(p, cb, s);
 }
 
 }  // namespace qlora

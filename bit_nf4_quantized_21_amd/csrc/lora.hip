@@ -267,16 +267,22 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
 // P[c][j][m] has RP rows per chunk.
 // ---------------------------------------------------------------------------
 template <int JT>
-__global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __restrict__ M,
-                                                             const uint16_t* __restrict__ Sh,
-                                                             const uint16_t* __restrict__ Sl, int64_t TP,
-                                                             float* __restrict__ P, int64_t T, int64_t C,
-                                                             int64_t TC) {
+__global__ __launch_bounds__(256) void tokdot_partial_kernel(TokJob j0, TokJob j1, int nwg0, int64_t TP,
+                                                             int64_t T) {
   __shared__ __align__(16) float red[4][64 * 64];
   constexpr int RP = 16 * JT;
+  // Workgroups [0, nwg0) serve job 0, the rest job 1 (uniform per workgroup).
+  const bool second = (int)blockIdx.x >= nwg0;
+  const int bid = second ? (int)blockIdx.x - nwg0 : (int)blockIdx.x;
+  const TokJob& jb = second ? j1 : j0;
+  const uint16_t* __restrict__ M = jb.M;
+  const uint16_t* __restrict__ Sh = jb.Sh;
+  const uint16_t* __restrict__ Sl = jb.Sl;
+  float* __restrict__ P = jb.P;
+  const int64_t C = jb.C, TC = jb.TC;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int64_t ch = blockIdx.y;
+  const int64_t m0 = (int64_t)(bid % jb.mtiles) * 64;
+  const int64_t ch = bid / jb.mtiles;
   const int64_t tbeg = ch * TC;
   const int64_t tend = tbeg + TC < T ? tbeg + TC : T;
   const int64_t TW = TC / 4;
@@ -376,12 +382,21 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(const uint16_t* __r
 // out = bf16(s * sum over chunks of P[c][j][m]), stored [j][m] (dB: [r,N]) or
 // [m][j] (dA: [K,r]).  Workgroup = a 64 j x 16 m tile; thread q handles 4
 // consecutive m of one j.
-__global__ __launch_bounds__(256) void tokdot_reduce_kernel(const float* __restrict__ P, uint16_t* __restrict__ out,
-                                                            int64_t C, int r, int RP, int nc, float s,
-                                                            int m_major) {
+__global__ __launch_bounds__(256) void tokdot_reduce_kernel(TokJob j0, TokJob j1, int nwg0, int r, int RP) {
+  // Workgroups [0, nwg0) serve job 0, the rest job 1 (uniform per workgroup).
+  const bool second = (int)blockIdx.x >= nwg0;
+  const int bid = second ? (int)blockIdx.x - nwg0 : (int)blockIdx.x;
+  const TokJob& job = second ? j1 : j0;
+  const float* __restrict__ P = job.P;
+  uint16_t* __restrict__ out = job.out;
+  const int64_t C = job.C;
+  const int nc = job.nc;
+  const float s = job.scale;
+  const int m_major = job.m_major;
+  const int mt16 = (int)((C + 15) / 16);
   __shared__ __align__(16) uint16_t tr[16 * 72];  // [m][j], j padded to 72
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int jb = blockIdx.y;
+  const int64_t m0 = (int64_t)(bid % mt16) * 16;
+  const int jb = bid / mt16;
   const int q = threadIdx.x;
   const int j = q >> 2, m4 = 4 * (q & 3);
   const int jg = 64 * jb + j;
@@ -451,23 +466,28 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float*
   return hipGetLastError();
 }
 
-hipError_t launch_tokdot(const uint16_t* M, const uint16_t* Sh, const uint16_t* Sl, int64_t TP, float* P,
-                         uint16_t* out, int64_t T, int64_t C, int r, int64_t TC, float scale, bool m_major,
-                         hipStream_t s) {
-  const int64_t nc = cdiv(T, TC);
+hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s) {
+  TokJob j[2] = {a, b};
+  int nwg[2];
+  for (int i = 0; i < 2; ++i) {
+    j[i].nc = (int)cdiv(T, j[i].TC);
+    j[i].mtiles = (int)cdiv(j[i].C, 64);
+    nwg[i] = j[i].mtiles * j[i].nc;
+  }
   const int JT = cdiv(r, 16) <= 4 ? 4 : 8;
-  dim3 grid((unsigned)cdiv(C, 64), (unsigned)nc);
   {
     KernelTimer kt_("tokdot_partial_kernel", s);
-    if (JT == 4) hipLaunchKernelGGL(tokdot_partial_kernel<4>, grid, dim3(256), 0, s, M, Sh, Sl, TP, P, T, C, TC);
-    else hipLaunchKernelGGL(tokdot_partial_kernel<8>, grid, dim3(256), 0, s, M, Sh, Sl, TP, P, T, C, TC);
+    const unsigned grid = (unsigned)(nwg[0] + nwg[1]);
+    if (JT == 4) hipLaunchKernelGGL(tokdot_partial_kernel<4>, dim3(grid), dim3(256), 0, s, j[0], j[1], nwg[0], TP, T);
+    else hipLaunchKernelGGL(tokdot_partial_kernel<8>, dim3(grid), dim3(256), 0, s, j[0], j[1], nwg[0], TP, T);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("tokdot_reduce_kernel", s);
-    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)cdiv(C, 16), (unsigned)cdiv(r, 64)), dim3(256), 0, s, P,
-                       out, C, r, 16 * JT, (int)nc, scale, m_major ? 1 : 0);
+    const int jbs = (int)cdiv(r, 64);
+    const int r0 = (int)cdiv(j[0].C, 16) * jbs, r1 = (int)cdiv(j[1].C, 16) * jbs;
+    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)(r0 + r1)), dim3(256), 0, s, j[0], j[1], r0, r, 16 * JT);
   }
   return hipGetLastError();
 }

@@ -34,12 +34,25 @@ struct RowdotOut {
 hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
                          int64_t L, int r, int64_t LC, hipStream_t s);
 
-// out = bf16(scale * M[T,C]^T S[T,r]) stored [r,C] (or [C,r] when m_major),
-// with S given as hi / lo tokdot planes (RowdotOut).  P is scratch of
-// ceil(T/TC) * RP * C floats; TC a multiple of 128.
-hipError_t launch_tokdot(const uint16_t* M, const uint16_t* Sh, const uint16_t* Sl, int64_t TP, float* P,
-                         uint16_t* out, int64_t T, int64_t C, int r, int64_t TC, float scale, bool m_major,
-                         hipStream_t s);
+// One tokdot: out = bf16(scale * M[T,C]^T S[T,r]) stored [r,C] (or [C,r]
+// when m_major), with S given as hi / lo tokdot planes (RowdotOut).  P is
+// scratch of ceil(T/TC) * RP * C floats; TC a multiple of 128.  nc and
+// mtiles are filled by the launcher.
+struct TokJob {
+  const uint16_t* M;
+  const uint16_t* Sh;
+  const uint16_t* Sl;
+  float* P;
+  uint16_t* out;
+  int64_t C, TC;
+  float scale;
+  int m_major;
+  int nc, mtiles;
+};
+
+// Two tokdots over the same T tokens and rank r in one launch of the partial
+// kernel and one of the reduction (their grids concatenated).
+hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s);
 
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t s);
 
