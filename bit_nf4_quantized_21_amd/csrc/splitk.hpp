@@ -24,6 +24,52 @@ namespace qlora {
 constexpr int kSplitSlotFloats = 256 * 256;  // one tile of fp32 partials
 constexpr int kCachePolicySystem = 1 | 16;   // sc0 | sc1
 
+// Adds the partials of the other S - 1 slots (NO >= S - 1 of them) to acc,
+// summing every element in slot order with this slot's own value at
+// position sidx.  The 16-byte chunks are read KB at a time with the loads of
+// all slots of a batch in flight together: one memory round trip per batch,
+// not per chunk.
+template <int NO, int KB, int NA, int NB, int NT = 256>
+__device__ __forceinline__ void splitk_add_slots(f32x16 (&acc)[NA][NB], rsrc_t rs, int S, int sidx) {
+  constexpr int kChunks = NA * NB * 4;
+  static_assert(kChunks % KB == 0, "batch");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int c0 = 0; c0 < kChunks; c0 += KB) {
+    u32x4 v[NO][KB];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) {
+      const int s = k < sidx ? k : k + 1;  // k-th slot other than sidx
+      if (s < S) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          const uint32_t off = (uint32_t)(s * kSplitSlotFloats * 4 + ((c0 + i) * NT + tid) * 16);
+          v[k][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0,
+                                                                                     kCachePolicySystem));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int c = c0 + i, a = c / (NB * 4), b = (c / 4) % NB, e4 = c % 4;
+      float sum[4];
+#pragma unroll
+      for (int s = 0; s <= NO; ++s) {
+        if (s >= S) break;  // uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float other = __uint_as_float(s < sidx ? v[s < NO ? s : NO - 1][i][e] : v[s > 0 ? s - 1 : 0][i][e]);
+          const float x = s == sidx ? acc[a][b][4 * e4 + e] : other;
+          sum[e] = s == 0 ? x : sum[e] + x;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[a][b][4 * e4 + e] = sum[e];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batches apart (registers)
+  }
+}
+
 // Returns true in the workgroup that must finish the tile (acc then holds the
 // full sum); false in the others, which must exit without storing.  Called by
 // all NT threads of the workgroup; flag is one int of LDS.  `ticket` and
@@ -66,35 +112,7 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const uint32_t off = (uint32_t)((((a * NB + b) * 4 + e4) * NT + tid) * 16);
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < S; ++s) {
-          float4 v;
-          if (s == sidx) {
-            v = make_float4(acc[a][b][4 * e4], acc[a][b][4 * e4 + 1], acc[a][b][4 * e4 + 2], acc[a][b][4 * e4 + 3]);
-          } else {
-            const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          rs, (int)((uint32_t)s * kSplitSlotFloats * 4 + off), 0,
-                                                          kCachePolicySystem));
-            v = make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3]));
-          }
-          if (s == 0) {
-            sum = v;
-          } else {
-            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-          }
-        }
-        acc[a][b][4 * e4] = sum.x;
-        acc[a][b][4 * e4 + 1] = sum.y;
-        acc[a][b][4 * e4 + 2] = sum.z;
-        acc[a][b][4 * e4 + 3] = sum.w;
-      }
+  splitk_add_slots<3, 8>(acc, rs, S, sidx);
   if (tid == 0) {
     __hip_atomic_exchange(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_exchange(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
