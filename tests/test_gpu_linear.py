@@ -183,6 +183,18 @@ def test_33b_65b_linears_full_size_sampled(N, K, T):
     _check(c, out, rows=rows)
 
 
+def test_three_slice_split_tiles():
+    """72 tiles of 256 x 256 (9 per XCD) in both GEMMs: the last round cuts
+    every tile into three contraction slices, so the combine adds two other
+    slices' partials in slice order."""
+    print("three-slice split", flush=True)
+    c = Case(2304, 2304, 2048, 16, seed=23)
+    out = c.gpu()
+    rows = np.random.Generator(np.random.PCG64(5)).choice(2048, 30, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, 255, 256, 2047]]))
+    _check(c, out, rows=rows)
+
+
 def test_zero_adapter_and_zero_weight():
     """B = 0 leaves the base output and gives dA = 0; W = 0 isolates the adapter."""
     c = Case(256, 256, 40, 8, seed=3)
