@@ -56,6 +56,7 @@ constexpr int kLut = 3072;       // codebook pair table at address 0, 16-entry c
 constexpr int kW0 = kLut, kW1 = kW0 + kBuf, kD0 = kW1 + kBuf, kD1 = kD0 + kBuf, kS0 = kD1 + kBuf;
 constexpr int kSBytes = 4 * 64 * 4;  // [4 k-blocks][64 rows] fp32 scales
 constexpr int kSmem = kS0 + 2 * kSBytes;
+constexpr int kCodeStage = 64 * 128;  // raw codes of a step: 64 rows x 256 k
 static_assert(kS0 >= 256 * 512, "the dX staging tile fits below the scale tables");
 
 // Calls f(integral_constant<int, I0 + i>) for i = 0, 1, ...: one straight-line
@@ -73,6 +74,9 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
 
 __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codebook cb) {
   __shared__ __align__(1024) unsigned char smem[kSmem];
+  // Raw code tiles of two steps, each its own object so the compiler can
+  // tell the stage being filled by buffer-to-LDS loads from the one read.
+  __shared__ __align__(1024) unsigned char cst0[kCodeStage], cst1[kCodeStage];
   const int tid = threadIdx.x;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; each XCD works
@@ -116,10 +120,26 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   const rsrc_t rd = make_rsrc(p.dY + t0 * N, (T - t0) * N * 2);
   const uint32_t coff = (uint32_t)((8 * rg) * K2 + kcol / 2);
   auto load_code = [&](int j, int i) -> uint32_t { return buf_load4(rc, coff + (uint32_t)(j * 64 * K2 + i * K2)); };
-  // q8 of this thread's scale entry (zero for a k-block past K) and its s2.
+  // Codes of later steps go through LDS: wave w copies rows 16w .. 16w+15
+  // of a step (two buffer-to-LDS loads of 8 rows x 128 bytes, load q taking
+  // rows 16w + 8q ..) and later reads only those rows, so no barrier orders
+  // the copy.  Physical row pr holds row pr ^ ((pr >> 3) & 1): the two rows
+  // a wave reads at once (8 apart) sit in opposite halves of the banks.
+  const int crow = lane >> 3, cchunk = lane & 7;
+  auto dma_codes = [&](unsigned char* st, int j, int q) {
+    const int lr = (16 * wave + 8 * q + crow) ^ q;
+    buf_load16_to_lds(rc, st + (16 * wave + 8 * q) * 128,
+                      (uint32_t)(((int64_t)j * 64 + lr) * K2 + k0 / 2 + 16 * cchunk));
+  };
+  auto read_code = [&](const unsigned char* st, int i) -> uint32_t {
+    const int lr = 8 * rg + i, pr = lr ^ ((lr >> 3) & 1);
+    return *reinterpret_cast<const uint32_t*>(st + pr * 128 + 4 * kq);
+  };
+  // q8 of this thread's scale entry (zero for a k-block past K: its offset
+  // is pushed out of the view, so no select has to wait for the load) and
+  // its s2.
   auto load_q = [&](int j) -> uint32_t {
-    const uint32_t q = buf_load1(rq, (uint32_t)(((int64_t)j * 64 + sr) * bpr + skb));
-    return sval ? q : 0u;
+    return buf_load1(rq, off_if(sval, (uint32_t)(((int64_t)j * 64 + sr) * bpr + skb)));
   };
   auto load_s = [&](int j) -> float {
     const int64_t b = ((int64_t)j * 64 + sr) * bpr + skb;
@@ -198,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
       }                                                                                                \
     }                                                                                                  \
   }
-#define QLORA_DX_SLICE(I, MF, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                                    \
+#define QLORA_DX_SLICE(I, MF, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS, CR, CD)                                    \
   {                                                                                                    \
     const int I_ = (I), s_ = I_ >> 4, i_ = I_ & 15;                                                    \
     if (I_ == 50) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                      \
@@ -218,7 +238,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
     if (I_ >= 43 && I_ < 47) write_col(WN, 1, I_ - 43, col[1][I_ - 43]);                                \
     if (I_ >= 24 && I_ < 32) store_row(DN, I_ - 24, dyr[I_ - 24]);                                     \
     if (I_ >= 32 && I_ < 40) dyr[I_ - 32] = load_dy((J) + 2, I_ - 32);                                 \
-    if (I_ < 8) CF[I_] = load_code((J) + 2, I_);                                                       \
+    if (I_ < 2) dma_codes(CD, (J) + 3, I_);                                                            \
+    if (I_ == 50 || I_ == 51) {                                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) CF[4 * (I_ - 50) + i_] = read_code(CR, 4 * (I_ - 50) + i_); \
+    }                                                                                                  \
     if (I_ == 8) qv[QL] = load_q((J) + 3);                                                             \
     if (I_ == 9) s2v[QL] = load_s((J) + 3);                                                            \
     if (I_ == 28) sfv = dq_scale(qv[QS], s2v[QS]);                                                     \
@@ -229,12 +252,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // scale table SN holds W'(J+1)'s scales, SF receives W'(J+2)'s; CN holds
   // codes(J+1), CF receives codes(J+2); q8/s2 of step J+3 go to set QL, the
   // set QS (loaded one step earlier) gives W'(J+2)'s scale.
-#define QLORA_DX_STEP(J, I0, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                                    \
+#define QLORA_DX_STEP(J, I0, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS, CR, CD)                                    \
   {                                                                                                    \
     float sfv = 0.0f;                                                                                  \
     auto slice_ = [&](auto ic_) __attribute__((always_inline)) {                                       \
       constexpr int I = decltype(ic_)::value;                                                          \
-      QLORA_DX_SLICE(I, (I0) == 0, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS)                          \
+      QLORA_DX_SLICE(I, (I0) == 0, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS, CR, CD)                          \
     };                                                                                                 \
     run_slices<(I0)>(slice_, std::make_integer_sequence<int, 64 - (I0)>{});                            \
     (void)sfv;                                                                                         \
@@ -250,8 +273,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
     uint32_t c0[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) c0[i] = load_code(jbeg, i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cB[i] = load_code(jbeg + 1, i);
+    dma_codes(cst1, jbeg + 1, 0);
+    dma_codes(cst1, jbeg + 1, 1);
+    dma_codes(cst0, jbeg + 2, 0);
+    dma_codes(cst0, jbeg + 2, 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dyr[i] = load_dy(jbeg, i);
     *scale_slot(0) = dq_scale(load_q(jbeg), load_s(jbeg));
@@ -283,15 +308,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
     for (int i = 0; i < 8; ++i) dyr[i] = load_dy(jbeg + 1, i);
     __syncthreads();  // W'(jbeg), dY(jbeg) complete
   }
-  QLORA_DX_STEP(jbeg - 1, 50, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 0, 1)
+  QLORA_DX_STEP(jbeg - 1, 50, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 0, 1, cst1, cst0)
 
   // Steps past jend only prefetch and decode data that is never used.
   int j = jbeg;
   for (; j + 2 <= jend; j += 2) {
-    QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1)
-    QLORA_DX_STEP(j + 1, 0, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 1, 0)
+    QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1, cst0, cst1)
+    QLORA_DX_STEP(j + 1, 0, kW1, kD1, kW0, kD0, 0, 1, cA, cB, 1, 0, cst1, cst0)
   }
-  if (j < jend) QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1)
+  if (j < jend) QLORA_DX_STEP(j, 0, kW0, kD0, kW1, kD1, 1, 0, cB, cA, 0, 1, cst0, cst1)
 #undef QLORA_DX_STEP
 #undef QLORA_DX_SLICE
 #undef QLORA_DX_DECODE_SLOT
