@@ -44,6 +44,11 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+__device__ __forceinline__ float4 buf_load_f4(rsrc_t r, uint32_t off) {
+  const u32x4 u = buf_load16(r, off);
+  return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3]));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -195,12 +200,16 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
     const int64_t tg = t0 + t;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tg < T) {
+      // The chunks' loads of a batch are issued together (chunks past nc
+      // read zero through an out-of-range offset, no branch), then added in
+      // chunk order.
+      const rsrc_t rp = make_rsrc(P, (int64_t)nc * T * RP * 4);
       float4 part[8];
       for (int c0 = 0; c0 < nc; c0 += 8) {
         const int n = nc - c0 < 8 ? nc - c0 : 8;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * T + tg) * RP + j);
+          part[c] = buf_load_f4(rp, off_if(c < n, (uint32_t)((((int64_t)(c0 + c) * T + tg) * RP + j) * 4)));
 #pragma unroll
         for (int c = 0; c < 8; ++c)
           if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
@@ -403,12 +412,15 @@ __global__ __launch_bounds__(256) void tokdot_reduce_kernel(TokJob j0, TokJob j1
   const int64_t mg = m0 + m4;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (jg < r && mg < C) {
+    // Loads of a batch issued together (past nc: zero, no branch), then
+    // added in chunk order.
+    const rsrc_t rp = make_rsrc(P, (int64_t)nc * RP * C * 4);
     float4 part[8];
     for (int c0 = 0; c0 < nc; c0 += 8) {
       const int n = nc - c0 < 8 ? nc - c0 : 8;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        if (c < n) part[c] = *reinterpret_cast<const float4*>(P + ((int64_t)(c0 + c) * RP + jg) * C + mg);
+        part[c] = buf_load_f4(rp, off_if(c < n, (uint32_t)((((int64_t)(c0 + c) * RP + jg) * C + mg) * 4)));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         if (c < n) v = (c0 + c == 0) ? part[c] : add4(v, part[c]);
