@@ -17,6 +17,15 @@ it was measured on) and a readable profiles/traffic_<workload>.md.
 
 `stats` turns a `rocprofv3 --kernel-trace --stats --output-format csv` kernel
 statistics file into a short markdown table.
+
+`mfma` summarises a third counter pass,
+
+    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d OUT/mfma -o mfma -- \
+        python bit_nf4_quantized_21_amd/profile_run.py run
+
+into profiles/mfma_mlp7b_gemv7b.md: per kernel the share of SIMD cycles with
+the matrix cores busy (MfmaUtil, percent) and the bf16 MFMA flops executed
+per launch beside the algorithmic flops.
 """
 
 from __future__ import annotations
@@ -71,6 +80,16 @@ def algorithmic_bytes(kernel, T, N, K, r):
         return 2 * T * N + dq_bytes(N, K) + 2 * K * r + 4 * T * r + 2 * T * K
     if kernel == "gemv_fwd_kernel":
         return 2 * T * K + dq_bytes(N, K) + 2 * r * N + 4 * T * r + 2 * T * N
+    return None
+
+
+def algorithmic_flops(kernel, T, N, K, r):
+    if kernel == "gemm_fwd_kernel":
+        return 2 * T * N * K + 2 * T * r * N
+    if kernel == "gemm_dx_kernel":
+        return 2 * T * N * K + 2 * T * r * K
+    if kernel == "gemv_fwd_kernel":
+        return 2 * T * N * K + 2 * T * r * N
     return None
 
 
@@ -195,6 +214,35 @@ def stats(stats_csv, out_md, command, top=12):
     print("\n".join(lines))
 
 
+def mfma(pmc_dir, command):
+    util, flops = read_counter(pmc_dir, "MfmaUtil"), read_counter(pmc_dir, "MfmaFlopsBF16")
+    kernels = list(KERNEL_SOURCES) + ["xa_partial_kernel", "rowdot_reduce_kernel", "tokdot_reduce_kernel"]
+    lines = ["# MFMA utilisation per kernel (rocprofv3 MfmaUtil, MfmaFlopsBF16)", "",
+             "Command (from the repository root):", "", "```", command, "```", "",
+             "MfmaUtil: SIMD cycles with the matrix core busy over active cycles x SIMDs, averaged over "
+             "launches. Flops: bf16 MFMA flops executed per launch (padding included) beside the "
+             "algorithmic flops of the workload's launches.", "",
+             "| kernel | workload | launches | MfmaUtil % | MFMA GFLOP/launch | algorithmic GFLOP/launch |",
+             "|---|---|---|---|---|---|"]
+    for kernel in kernels:
+        u = [v for (k, g, v) in util if short_name(k) == kernel]
+        f = [v for (k, g, v) in flops if short_name(k) == kernel]
+        if not u:
+            continue
+        wl = KERNEL_SOURCES.get(kernel, ("mlp7b" if "gemv" not in kernel and "xa_" not in kernel else "gemv7b",))[0]
+        if wl == "mlp7b":
+            alg = [algorithmic_flops(kernel, T_MLP, N, K, R) for (_, N, K) in MLP]
+        else:
+            alg = [algorithmic_flops(kernel, *GEMV, R)]
+        algs = "" if alg[0] is None else f"{sum(alg) / len(alg) / 1e9:.1f}"
+        fs = f"{sum(f) / len(f) / 1e9:.1f}" if f else ""
+        lines.append(f"| {kernel} | {wl} | {len(u)} | {sum(u) / len(u):.1f} | {fs} | {algs} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "mfma_mlp7b_gemv7b.md"), "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -204,6 +252,9 @@ def main():
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("--command", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("--command", required=True)
     s = sub.add_parser("stats")
     s.add_argument("stats_csv")
     s.add_argument("out_md")
@@ -213,6 +264,8 @@ def main():
         run(a.steps)
     elif a.cmd == "traffic":
         traffic(a.fetch_dir, a.write_dir, a.command)
+    elif a.cmd == "mfma":
+        mfma(a.pmc_dir, a.command)
     else:
         stats(a.stats_csv, a.out_md, a.command)
 
