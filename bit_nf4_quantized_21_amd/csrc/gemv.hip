@@ -11,9 +11,10 @@
 // bytes and the 8 partial sums are reduced through LDS at the end.  Each lane
 // owns one row and 32 consecutive k of a chunk (16 code bytes, one 16-byte
 // load); the codes are decoded in registers straight into the A operand of a
-// bf16 16x16x32 MFMA whose B operand is X padded to 16 token columns.  Loads
-// are issued four chunks ahead of the decode, the first four before anything
-// else, so a wave keeps ~16 KB of traffic in flight.
+// bf16 16x16x32 MFMA whose B operand is X padded to 16 token columns.  Each
+// wave keeps two chunks in flight (the loads of chunk c + 16 are issued as
+// soon as chunk c is decoded); deeper rings measured no faster at 4096 x
+// 4096 and slower for larger N, where two workgroups share a compute unit.
 //
 // The adapter's down-projection XA = X A comes from a small kernel launched
 // just before (xa_partial_kernel: workgroup b sums a slice of the
