@@ -41,6 +41,28 @@ def test_quantize_bit_exact(n):
     assert np.array_equal(s2.cpu().numpy().view(np.uint32), os2.view(np.uint32))
 
 
+def test_quantize_largest_linear_sampled_groups():
+    """The largest linear of the 65B set (22016 x 8192, 180 M weights) in one
+    call; 48 double-quant groups (256 blocks, 16384 weights each, so a group
+    is self-contained) at random positions plus the first and the last are
+    checked bit-exact against the oracle run on those groups alone."""
+    N, K = 22016, 8192
+    n = N * K
+    print(f"quantize n={n}", flush=True)
+    w = _rng(77).normal(0, 0.02, n).astype(np.float32)
+    codes, absmax, q8, s2 = _gpu_quant_all(w)
+    codes, absmax, q8, s2 = codes.cpu().numpy(), absmax.cpu().numpy(), q8.cpu().numpy(), s2.cpu().numpy()
+    gsz = 64 * 256
+    ng = n // gsz
+    groups = np.concatenate([[0, ng - 1], _rng(78).choice(np.arange(1, ng - 1), 48, replace=False)])
+    for g in groups:
+        oc, oq8, os2, oa = nf4.quantize_all(w[g * gsz:(g + 1) * gsz])
+        assert np.array_equal(codes[g * gsz // 2:(g + 1) * gsz // 2], oc), g
+        assert np.array_equal(absmax[g * 256:(g + 1) * 256].view(np.uint32), oa.view(np.uint32)), g
+        assert np.array_equal(q8[g * 256:(g + 1) * 256], oq8), g
+        assert np.array_equal(s2[g:g + 1].view(np.uint32), os2.view(np.uint32)), g
+
+
 def test_quantize_specials_and_ties():
     m = nf4.midpoints()
     rep = [j for j in range(15) if float(np.float32(m[j])) == m[j]]
