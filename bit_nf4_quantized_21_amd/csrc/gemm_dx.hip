@@ -201,11 +201,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // the issue order stays interleaved.
 #define QLORA_DX_DECODE_SLOT(U, CODES)                                                                  \
   {                                                                                                    \
-    const int U_ = (U);                                                                                \
-    const int g_ = (2 * U_ + 2) / 3;                                                                   \
-    if (U_ >= 0 && g_ < 32 && (3 * g_) / 2 == U_) {                                                    \
-      const int u_ = g_ >> 2, w_ = g_ & 3, hf_ = u_ >> 2, pr_ = u_ & 3;                                \
-      const int rs_ = w_ >> 1, b_ = w_ & 1;                                                            \
+    constexpr int U_ = (U);                                                                            \
+    constexpr int g_ = (2 * U_ + 2) / 3;                                                               \
+    if constexpr (U_ >= 0 && g_ < 32 && (3 * g_) / 2 == U_) {                                          \
+      constexpr int u_ = g_ >> 2, w_ = g_ & 3, hf_ = u_ >> 2, pr_ = u_ & 3;                            \
+      constexpr int rs_ = w_ >> 1, b_ = w_ & 1;                                                        \
       const float2 v_ = *reinterpret_cast<const float2*>(smem + byte_x8(CODES[2 * pr_ + rs_], 2 * hf_ + b_)); \
       fp[u_][4 * rs_ + 2 * b_] = v_.x;                                                                 \
       fp[u_][4 * rs_ + 2 * b_ + 1] = v_.y;                                                             \
@@ -214,38 +214,38 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
       const int c_ = U_ - (6 * u_ + 8);                                                                \
       if (c_ >= 0 && c_ < 4) {                                                                         \
         const int pr_ = u_ & 3;                                                                        \
-        col[u_ >> 2][c_][pr_] = pack_bf16x2(fp[u_][c_] * sc[2 * pr_], fp[u_][4 + c_] * sc[2 * pr_ + 1]); \
+        col[u_ >> 2][c_ & 3][pr_] = pack_bf16x2(fp[u_][c_ & 3] * sc[2 * pr_], fp[u_][4 + (c_ & 3)] * sc[2 * pr_ + 1]); \
       }                                                                                                \
     }                                                                                                  \
   }
 #define QLORA_DX_SLICE(I, MF, J, WB, DB, WN, DN, SN, SF, CN, CF, QL, QS, CR, CD)                                    \
   {                                                                                                    \
-    const int I_ = (I), s_ = I_ >> 4, i_ = I_ & 15;                                                    \
-    if (I_ == 50) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                      \
-    if (MF) acc[i_ >> 2][i_ & 3] = mfma32(oa[s_ & 1][i_ >> 2], ob[s_ & 1][i_ & 3], acc[i_ >> 2][i_ & 3]); \
-    if (s_ < 3 && i_ < 8) {                                                                            \
+    constexpr int I_ = (I), s_ = I_ >> 4, i_ = I_ & 15;                                                \
+    if constexpr (I_ == 50) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                      \
+    if constexpr (MF) acc[i_ >> 2][i_ & 3] = mfma32(oa[s_ & 1][i_ >> 2], ob[s_ & 1][i_ & 3], acc[i_ >> 2][i_ & 3]); \
+    if constexpr (s_ < 3 && i_ < 8) {                                                                            \
       const bf16x8 v_ = read_op(WB, DB, s_ + 1, i_);                                                   \
-      if (i_ < 4) ob[(s_ + 1) & 1][i_] = v_; else oa[(s_ + 1) & 1][i_ - 4] = v_;                        \
+      if constexpr (i_ < 4) ob[(s_ + 1) & 1][i_] = v_; else oa[(s_ + 1) & 1][i_ - 4] = v_;                        \
     }                                                                                                  \
-    if (I_ >= 50 && I_ < 58) {                                                                         \
+    if constexpr (I_ >= 50 && I_ < 58) {                                                                         \
       const bf16x8 v_ = read_op(WN, DN, 0, I_ - 50);                                                   \
-      if (I_ - 50 < 4) ob[0][I_ - 50] = v_; else oa[0][I_ - 54] = v_;                                   \
+      if constexpr (I_ - 50 < 4) ob[0][I_ - 50] = v_; else oa[0][I_ - 54] = v_;                                   \
     }                                                                                                  \
-    if (I_ == 56 || I_ == 57) read_scales(SF, I_ - 56, sc);                                            \
-    if (I_ + 12 >= 12 && I_ + 12 < 54) QLORA_DX_DECODE_SLOT(I_ + 12, CN)                                \
-    if (I_ >= 52) QLORA_DX_DECODE_SLOT(I_ - 52, CF)                                                    \
-    if (I_ >= 19 && I_ < 23) write_col(WN, 0, I_ - 19, col[0][I_ - 19]);                                \
-    if (I_ >= 43 && I_ < 47) write_col(WN, 1, I_ - 43, col[1][I_ - 43]);                                \
-    if (I_ >= 24 && I_ < 32) store_row(DN, I_ - 24, dyr[I_ - 24]);                                     \
-    if (I_ >= 32 && I_ < 40) dyr[I_ - 32] = load_dy((J) + 2, I_ - 32);                                 \
-    if (I_ < 2) dma_codes(CD, (J) + 3, I_);                                                            \
-    if (I_ == 50 || I_ == 51) {                                                                        \
-      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) CF[4 * (I_ - 50) + i_] = read_code(CR, 4 * (I_ - 50) + i_); \
+    if constexpr (I_ == 56 || I_ == 57) read_scales(SF, I_ - 56, sc);                                            \
+    if constexpr (I_ + 12 >= 12 && I_ + 12 < 54) QLORA_DX_DECODE_SLOT(I_ + 12, CN)                                \
+    if constexpr (I_ >= 52) QLORA_DX_DECODE_SLOT(I_ - 52, CF)                                                    \
+    if constexpr (I_ >= 19 && I_ < 23) write_col(WN, 0, I_ - 19, col[0][I_ - 19]);                                \
+    if constexpr (I_ >= 43 && I_ < 47) write_col(WN, 1, I_ - 43, col[1][I_ - 43]);                                \
+    if constexpr (I_ >= 24 && I_ < 32) store_row(DN, I_ - 24, dyr[I_ - 24]);                                     \
+    if constexpr (I_ >= 32 && I_ < 40) dyr[I_ - 32] = load_dy((J) + 2, I_ - 32);                                 \
+    if constexpr (I_ < 2) dma_codes(CD, (J) + 3, I_);                                                            \
+    if constexpr (I_ == 50 || I_ == 51) {                                                              \
+      _Pragma("unroll") for (int ii_ = 0; ii_ < 4; ++ii_) CF[4 * (I_ - 50) + ii_] = read_code(CR, 4 * (I_ - 50) + ii_); \
     }                                                                                                  \
-    if (I_ == 8) qv[QL] = load_q((J) + 3);                                                             \
-    if (I_ == 9) s2v[QL] = load_s((J) + 3);                                                            \
-    if (I_ == 28) sfv = dq_scale(qv[QS], s2v[QS]);                                                     \
-    if (I_ == 30) *scale_slot(SF) = sfv;                                                               \
+    if constexpr (I_ == 8) qv[QL] = load_q((J) + 3);                                                             \
+    if constexpr (I_ == 9) s2v[QL] = load_s((J) + 3);                                                            \
+    if constexpr (I_ == 28) sfv = dq_scale(qv[QS], s2v[QS]);                                                     \
+    if constexpr (I_ == 30) *scale_slot(SF) = sfv;                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                                 \
   }
   // Step J on buffers WB/DB (W'(J), dY(J)); WN/DN receive W'(J+1), dY(J+1);
