@@ -15,7 +15,8 @@ Beside it, in the same JSON line:
   gemv          the small-token forward (LLaMA-7B q_proj 4096x4096, 4 tokens,
                 r=64): dequant-GEMV kernel GB/s over 40 rotating weight copies
                 (> 256 MB, so every launch streams the 4-bit weights from HBM);
-  quantize      blockwise NF4 quantization + double quantization GB/s;
+  quantize      blockwise NF4 quantization (fp32 and bf16 weights) + double
+                quantization GB/s;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload mlp7b|layer33b|tiny]
@@ -244,6 +245,22 @@ def bench_quantize(torch, qlora, iters=10):
            "quantize": {"avg_us": round(q_us, 2), "GBs": round(qbytes / (q_us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(qbytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": qbytes},
            "double_quant": {"avg_us": round(d_us, 2), "GBs": round(dbytes / (d_us * 1e-6) / 1e9, 1), "bytes": dbytes}}
+    # The same weights stored as bf16 (how pretrained checkpoints ship).
+    srcs = [x.to(torch.bfloat16) for x in srcs]
+    for i in range(4):
+        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
+    torch.cuda.synchronize()
+    qlora.timing_read()
+    qlora.timing_enable(True)
+    for i in range(iters):
+        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
+    torch.cuda.synchronize()
+    qlora.timing_enable(False)
+    bn, bt = qlora.timing_read()["quantize_nf4_bf16_kernel"]
+    bbytes = 2 * n + n // 2 + 4 * (n // 64)
+    b_us = bt * 1e3 / bn
+    res["quantize_bf16"] = {"avg_us": round(b_us, 2), "GBs": round(bbytes / (b_us * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(bbytes / (b_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": bbytes}
     del srcs
     torch.cuda.empty_cache()
     return res

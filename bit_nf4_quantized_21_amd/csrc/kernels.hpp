@@ -12,6 +12,8 @@ struct Midpoints;
 
 hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax,
                                const Midpoints& mp, hipStream_t s);
+hipError_t launch_quantize_nf4_bf16(const uint16_t* W, int64_t n, uint8_t* codes, float* absmax,
+                                    const Midpoints& mp, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* q8, float* s2, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
                              int out_bf16, void* out, const Codebook& cb, hipStream_t s);

@@ -96,6 +96,16 @@ int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize, uint8_t* co
   return hip_status(qlora::launch_quantize_nf4(W, n, codes, absmax, tables().mp, (hipStream_t)stream));
 }
 
+int qlora_quantize_nf4_bf16(const uint16_t* W, int64_t n, int32_t blocksize, uint8_t* codes, float* absmax,
+                            void* stream) {
+  if (blocksize != 64) return QLORA_ERR_UNSUPPORTED;
+  if (n < 0 || n % 2 != 0 || n > (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
+  if (n == 0) return QLORA_OK;
+  if (!W || !codes || !absmax) return QLORA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_quantize_nf4_bf16(W, n, codes, absmax, tables().mp, (hipStream_t)stream));
+}
+
 int qlora_double_quant(const float* absmax, int64_t nb, int32_t blocksize2, uint8_t* q8, float* s2,
                        void* stream) {
   if (blocksize2 != 256) return QLORA_ERR_UNSUPPORTED;

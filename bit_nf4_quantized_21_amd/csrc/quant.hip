@@ -33,9 +33,35 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double a64, const double* 
 }
 
 // Each 16-lane group quantizes kQGroupBlocks consecutive blocks; the loads of
-// all of them are issued before any is used, so a wave keeps 4 KiB of the
-// weight stream in flight.
+// all of them are issued before any is used, so a wave keeps 4 KiB (fp32) or
+// 2 KiB (bf16) of the weight stream in flight.  The per-weight decision work,
+// not the bytes, bounds these kernels, so bf16 weights keep the same grid
+// (8 blocks per group, half the waves, measured 13 % slower).
 constexpr int kQGroupBlocks = 4;
+
+// Four consecutive weights from e0 as fp32; zero past n.  A bf16 weight
+// widens to fp32 exactly (its bits are the upper half of the fp32 word), so
+// every decision below is the one taken for the same value given as fp32.
+__device__ __forceinline__ void load_weights4(const float* __restrict__ W, int64_t n, int64_t e0, float (&v)[4]) {
+  if (e0 + 4 <= n) {
+    const float4 x = *reinterpret_cast<const float4*>(W + e0);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+  }
+}
+__device__ __forceinline__ void load_weights4(const uint16_t* __restrict__ W, int64_t n, int64_t e0,
+                                              float (&v)[4]) {
+  if (e0 + 4 <= n) {
+    const uint2 x = *reinterpret_cast<const uint2*>(W + e0);
+    v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (e0 + i < n) ? __uint_as_float((uint32_t)W[e0 + i] << 16) : 0.0f;
+  }
+}
 constexpr int kBins = 128;             // uniform bins of w / absmax over [-1, 1]
 constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
 
@@ -45,9 +71,9 @@ constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
 // true position or is a neighbour separated from it by no boundary.  The code
 // is the number of boundaries below the bin plus the exact fp64 decision
 // w > absmax * m_j for the bin's own boundary (m = +inf when it has none).
-__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
-                                                           uint8_t* __restrict__ codes,
-                                                           float* __restrict__ absmax, Midpoints mp) {
+template <typename T>
+__device__ __forceinline__ void quantize_nf4_binned(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ absmax, const Midpoints& mp) {
   __shared__ double s_thr[kBins];
   __shared__ uint32_t s_lo[kBins];
   if (threadIdx.x < kBins) {
@@ -64,24 +90,15 @@ __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restri
   }
   __syncthreads();
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * kQGroupBlocks;
+  constexpr int G = kQGroupBlocks;
+  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * G;
   const int l16 = threadIdx.x & 15;
   if (blk0 >= nb) return;  // whole 16-lane groups leave together (after the barrier)
-  float v[kQGroupBlocks][4];
+  float v[G][4];
 #pragma unroll
-  for (int g = 0; g < kQGroupBlocks; ++g) {
-    const int64_t blk = blk0 + g;
-    const int64_t e0 = blk * kBlock + l16 * 4;
-    if (blk * kBlock + kBlock <= n) {
-      const float4 x = *reinterpret_cast<const float4*>(W + e0);
-      v[g][0] = x.x; v[g][1] = x.y; v[g][2] = x.z; v[g][3] = x.w;
-    } else {
+  for (int g = 0; g < G; ++g) load_weights4(W, n, (blk0 + g) * kBlock + l16 * 4, v[g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[g][i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < kQGroupBlocks; ++g) {
+  for (int g = 0; g < G; ++g) {
     const int64_t blk = blk0 + g;
     if (blk >= nb) break;  // uniform per 16-lane group
     const int64_t e0 = blk * kBlock + l16 * 4;
@@ -117,30 +134,34 @@ __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restri
   }
 }
 
+// One kernel per weight type, so that traces tell them apart.
+__global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ absmax,
+                                                           Midpoints mp) {
+  quantize_nf4_binned(W, n, codes, absmax, mp);
+}
+__global__ __launch_bounds__(256) void quantize_nf4_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ absmax, Midpoints mp) {
+  quantize_nf4_binned(W, n, codes, absmax, mp);
+}
+
 // Exact linear scan over the 15 boundaries (used when the bins above do not
 // separate the boundaries of the codebook in use).
-__global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const float* __restrict__ W, int64_t n,
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const T* __restrict__ W, int64_t n,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax, Midpoints mp) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * kQGroupBlocks;
+  constexpr int G = kQGroupBlocks;
+  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * G;
   const int l16 = threadIdx.x & 15;
   if (blk0 >= nb) return;  // whole 16-lane groups leave together
-  float v[kQGroupBlocks][4];
+  float v[G][4];
 #pragma unroll
-  for (int g = 0; g < kQGroupBlocks; ++g) {
-    const int64_t blk = blk0 + g;
-    const int64_t e0 = blk * kBlock + l16 * 4;
-    if (blk * kBlock + kBlock <= n) {
-      const float4 x = *reinterpret_cast<const float4*>(W + e0);
-      v[g][0] = x.x; v[g][1] = x.y; v[g][2] = x.z; v[g][3] = x.w;
-    } else {
+  for (int g = 0; g < G; ++g) load_weights4(W, n, (blk0 + g) * kBlock + l16 * 4, v[g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[g][i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < kQGroupBlocks; ++g) {
+  for (int g = 0; g < G; ++g) {
     const int64_t blk = blk0 + g;
     if (blk >= nb) break;  // uniform per 16-lane group
     const int64_t e0 = blk * kBlock + l16 * 4;
@@ -258,10 +279,14 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax,
-                               const Midpoints& mp, hipStream_t s) {
+namespace {
+template <typename T>
+hipError_t launch_quantize_nf4_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints),
+                                 const T* W, int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp,
+                                 const char* name, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t grid = (nb + 16 * kQGroupBlocks - 1) / (16 * kQGroupBlocks);
+  constexpr int G = kQGroupBlocks;
+  const int64_t grid = (nb + 16 * G - 1) / (16 * G);
   // The bins must hold at most one boundary each, none within 1e-5 of an edge.
   bool binned = true;
   for (int b = 0; b < kBins && binned; ++b) {
@@ -274,13 +299,26 @@ hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float*
     if (inside > 1) binned = false;
   }
   {
-    KernelTimer kt_("quantize_nf4_kernel", s);
+    KernelTimer kt_(name, s);
     if (binned)
-      hipLaunchKernelGGL(quantize_nf4_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+      hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
     else
-      hipLaunchKernelGGL(quantize_nf4_scan_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+      hipLaunchKernelGGL(quantize_nf4_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax,
+                         mp);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp,
+                               hipStream_t s) {
+  return launch_quantize_nf4_t(quantize_nf4_kernel, W, n, codes, absmax, mp, "quantize_nf4_kernel", s);
+}
+
+hipError_t launch_quantize_nf4_bf16(const uint16_t* W, int64_t n, uint8_t* codes, float* absmax,
+                                    const Midpoints& mp, hipStream_t s) {
+  return launch_quantize_nf4_t(quantize_nf4_bf16_kernel, W, n, codes, absmax, mp, "quantize_nf4_bf16_kernel",
+                               s);
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* q8, float* s2, hipStream_t s) {

@@ -101,6 +101,7 @@ def run(steps):
     layers = []
     for i, (_, N, K) in enumerate(MLP):
         inp = synth.device_inputs(T_MLP, N, K, R, i, backward=True)
+        qlora.quantize_nf4(inp["W"].view(-1).to(torch.bfloat16))  # the same weights stored as bf16
         codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
         q8, s2 = qlora.double_quant(absmax)
         del inp["W"], absmax

@@ -21,6 +21,7 @@ _c_i64, _c_i32, _c_p, _c_sz, _c_f = ctypes.c_int64, ctypes.c_int32, ctypes.c_voi
 
 _SIGNATURES = {
     "qlora_quantize_nf4": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
+    "qlora_quantize_nf4_bf16": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "qlora_double_quant": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "qlora_dequantize_nf4": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i32, _c_p, _c_p]),
     "qlora_linear_fwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
@@ -121,9 +122,10 @@ def nf4_codebook():
 
 
 def quantize_nf4(W, codes=None, absmax=None, stream=None):
-    """W: fp32 CUDA tensor (flattened row-major).  Returns (codes u8, absmax f32)."""
+    """W: fp32 or bf16 CUDA tensor (flattened row-major).  Returns (codes u8, absmax f32)."""
     torch = _torch()
-    _dev(W, torch.float32, "W")
+    bf16 = W.dtype == torch.bfloat16
+    _dev(W, torch.bfloat16 if bf16 else torch.float32, "W")
     n = W.numel()
     nb = (n + 63) // 64
     codes = torch.empty(n // 2, dtype=torch.uint8, device=W.device) if codes is None else codes
@@ -132,7 +134,8 @@ def quantize_nf4(W, codes=None, absmax=None, stream=None):
     _dev(absmax, torch.float32, "absmax")
     if codes.numel() < n // 2 or absmax.numel() < nb:
         raise ValueError("output buffers too small")
-    _check(lib().qlora_quantize_nf4(_p(W), n, 64, _p(codes), _p(absmax), _stream(stream)))
+    entry = lib().qlora_quantize_nf4_bf16 if bf16 else lib().qlora_quantize_nf4
+    _check(entry(_p(W), n, 64, _p(codes), _p(absmax), _stream(stream)))
     return codes, absmax
 
 

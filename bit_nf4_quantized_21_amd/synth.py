@@ -69,6 +69,12 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def from_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """The fp32 values that bf16 words encode: each word is the upper half of
+    the fp32 word, so the widening is exact."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def weight(N: int, K: int, i: int = 0) -> np.ndarray:
     return _rng(1000 + i).normal(0.0, 0.02, size=(N, K)).astype(np.float32)
 

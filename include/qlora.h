@@ -76,6 +76,19 @@ int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize,
                        uint8_t* codes, float* absmax, void* stream);
 
 /*
+ * The same blockwise NF4 quantization for weights stored as bf16, the 16-bit
+ * format in which pretrained base models ship (Abstract item (a); the
+ * quantizer is defined on real-valued weights).
+ *   W       [n]        bf16 weights (raw bits as uint16_t), the [N,K] matrix
+ *                      flattened row-major; 16-byte aligned.
+ * n, blocksize, codes, absmax and the error returns are those of
+ * qlora_quantize_nf4.  A bf16 value widens to fp32 exactly, so codes and
+ * absmax are bit-identical to qlora_quantize_nf4 on the fp32 widening of W.
+ */
+int qlora_quantize_nf4_bf16(const uint16_t* W, int64_t n, int32_t blocksize,
+                            uint8_t* codes, float* absmax, void* stream);
+
+/*
  * Double quantization of the absmax constants (Abstract item (b);
  * innovations list: quantizing the quantization constants saves ~0.37 bit
  * per parameter).

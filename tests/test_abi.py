@@ -59,6 +59,13 @@ def test_quantize_argument_errors(L):
     assert L.qlora_quantize_nf4(P, 128, 64, None, P, None) == ENULL
     assert L.qlora_quantize_nf4(MIS, 128, 64, P, P, None) == EALIGN
     assert L.qlora_quantize_nf4(None, 0, 64, None, None, None) == OK   # empty input: no-op
+    for f in (L.qlora_quantize_nf4_bf16,):
+        assert f(P, 128, 32, P, P, None) == EUNSUP
+        assert f(P, 127, 64, P, P, None) == ESHAPE
+        assert f(None, 128, 64, P, P, None) == ENULL
+        assert f(P, 128, 64, P, None, None) == ENULL
+        assert f(MIS, 128, 64, P, P, None) == EALIGN
+        assert f(None, 0, 64, None, None, None) == OK
 
 
 def test_double_quant_and_dequant_argument_errors(L):
