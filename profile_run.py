@@ -6,9 +6,9 @@ small-token forwards (4096x4096, 4 tokens), and a plain copy of a known number
 of bytes that calibrates the HBM byte counters:
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o fetch -- \
-        python bit_nf4_quantized_21_amd/profile_run.py run
+        python profile_run.py run
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o write -- \
-        python bit_nf4_quantized_21_amd/profile_run.py run
+        python profile_run.py run
 
 `traffic` turns the two counter CSVs into per-kernel HBM bytes per launch,
 scaled by what the same counters read for the copy, and writes
@@ -21,7 +21,7 @@ statistics file into a short markdown table.
 `mfma` summarises a third counter pass,
 
     rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d OUT/mfma -o mfma -- \
-        python bit_nf4_quantized_21_amd/profile_run.py run
+        python profile_run.py run
 
 into profiles/mfma_mlp7b_gemv7b.md: per kernel the share of SIMD cycles with
 the matrix cores busy (MfmaUtil, percent) and the bf16 MFMA flops executed
@@ -38,7 +38,7 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "bit_nf4_quantized_21_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 if ROOT not in sys.path:

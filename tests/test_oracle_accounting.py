@@ -1,5 +1,6 @@
 """Pins of the stored format and the layer's parameter counts against the
-figures the pages print (tests/golden/page_figures.json), and of NF4's
+figures the pages print (tests/golden/page_figures.json) and the workload
+descriptions state (tests/golden/workload_figures.json), and of NF4's
 quantization error against the Int4 and FP4 types the pages compare it with."""
 
 import json
@@ -11,6 +12,7 @@ import pytest
 from oracle import accounting, baselines, nf4
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+WORKLOAD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "workload_figures.json")))
 
 
 def test_bits_per_param_from_actual_outputs():
@@ -52,7 +54,7 @@ def test_lora_7b_rank8_size():
 
 
 def test_full65b_resident_size():
-    g = GOLD["full65b_resident_GB"]
+    g = WORKLOAD["full65b_resident_GB"]
     params = accounting.linear_params(*accounting.LLAMA["65B"])
     total = 0
     for (n, k) in [(8192, 8192)] * 4 + [(22016, 8192)] * 2 + [(8192, 22016)]:

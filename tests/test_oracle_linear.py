@@ -134,3 +134,32 @@ def test_merge_identity():
 
 def test_scale_values():
     assert lora.lora_scale(16.0, 8) == 2.0 and lora.lora_scale(16.0, 64) == 0.25
+
+
+@pytest.mark.parametrize("rows", [[0, 2, 3], [1], [3, 0]])
+def test_dx_rows_matches_loops_and_full_backward(rows):
+    """dx_rows (the dX reference for sampled token rows at full layer sizes)
+    equals the triple-loop dX and linear_bwd's dX on those rows, so a dropped
+    scale or a transposed factor in it would fail here."""
+    X, Wd, A, B, dY = _tiny(7, T=4, K=64, N=6, r=3)
+    alpha, r = 16.0, 3
+    s = lora.lora_scale(alpha, r)
+    got = lora.dx_rows(dY[rows], Wd, A, B, alpha, r)
+    dX, _, _, _ = lora.linear_bwd(dY, X, Wd, A, B, alpha, r)
+    ldX, _, _ = _loops_bwd(dY, X, Wd, A, B, s)
+    assert np.allclose(got, dX[rows], rtol=1e-13, atol=1e-14)
+    assert np.allclose(got, ldX[rows], rtol=1e-12, atol=1e-13)
+    # the adapter part alone carries the scale: with W' = 0 only s G A^T remains
+    got0 = lora.dx_rows(dY[rows], np.zeros_like(Wd), A, B, alpha, r)
+    G = dY[rows].astype(np.float64) @ B.astype(np.float64).T
+    assert np.allclose(got0, s * (G @ A.astype(np.float64).T), rtol=1e-13, atol=1e-15)
+    assert not np.allclose(got0, G @ A.astype(np.float64).T, rtol=1e-3)
+
+
+def test_forward_rows_match_full_forward():
+    """linear_fwd_rows on a subset of tokens equals those rows of the whole
+    forward (rows of Y and XA depend only on the same rows of X)."""
+    X, Wd, A, B, _ = _tiny(8, T=5)
+    Y, XA = lora.linear_fwd(X, Wd, A, B, 16.0, 2)
+    Yr, XAr = lora.linear_fwd_rows(X[[4, 1]], Wd, A, B, 16.0, 2)
+    assert np.array_equal(Yr, Y[[4, 1]]) and np.array_equal(XAr, XA[[4, 1]])
