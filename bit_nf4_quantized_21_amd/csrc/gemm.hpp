@@ -27,6 +27,7 @@ struct FwdGemmParams {
   float s;
   float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
   int* counters;         // 2 per split tile (tickets, then published counts), zero on entry, left zero
+  int* status;           // the device's status word (set if a split wait ran out)
   SplitPlan plan;        // filled by the launcher
   int tiles_n, tiles_m;  // filled by the launcher
 };
@@ -44,6 +45,7 @@ struct DxGemmParams {
   int r, RP;            // RP = r rounded up to 64
   float* slots;          // split partials: nsplit * S * 65536 floats (S > 1)
   int* counters;         // 2 per split tile (tickets, then published counts), zero on entry, left zero
+  int* status;           // the device's status word (set if a split wait ran out)
   SplitPlan plan;        // filled by the launcher
   int tiles_k, tiles_t;
 };

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
 
   if (it.S > 1 && !splitk_combine(acc, p.slots + (int64_t)it.ordinal * it.S * kSplitSlotFloats,
                                   p.counters + it.ordinal, p.counters + p.plan.nsplit() + it.ordinal, it.S, sidx,
-                                  reinterpret_cast<int*>(smem + kS0)))
+                                  reinterpret_cast<int*>(smem + kS0), p.status))
     return;
 
   // dX through LDS: D[k][t] of a 32x32 tile gives lane (l32, h) token

@@ -32,6 +32,9 @@ struct LinearArgs {
 };
 
 size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r);
+// True if every operand and workspace region of a T x K x N, rank-r problem
+// fits the kernels' 32-bit buffer views.
+bool linear_views_fit(int64_t T, int64_t K, int64_t N, int32_t r);
 size_t bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r);
 
 hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint16_t* X, uint16_t* Y, float* XA,

@@ -15,6 +15,7 @@
 // Every reduction is split into chunks whose partials are summed in a fixed
 // order, so results are bitwise reproducible.
 #include "common.hpp"
+#include "device_state.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
 #include "lora.hpp"
@@ -96,6 +97,23 @@ FwdLayout fwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   return l;
 }
 
+// Every kernel addresses its operands through buffer views whose size and
+// offsets are 32-bit (at most 2^31 - 1 bytes), so a problem is accepted only
+// if each operand and each workspace region fits one view.
+bool linear_views_fit(int64_t T, int64_t K, int64_t N, int32_t r) {
+  const int64_t lim = 0x7FFFFFFF;
+  const int64_t RP = rpad(r);
+  if (N * K / 2 > lim || T * K * 2 > lim || T * N * 2 > lim) return false;
+  if (K * RP * 2 > lim || RP * N * 2 > lim || T * RP * 4 > lim) return false;
+  if (T <= 0) return true;
+  const FwdLayout f = fwd_layout(T, K, N, r);
+  const BwdLayout b = bwd_layout(T, K, N, r);
+  const size_t regions[] = {f.p, f.xah, f.slots, b.pg, b.g, b.planes, b.ptok_b, b.ptok_a, b.slots};
+  for (size_t x : regions)
+    if (x > (size_t)lim) return false;
+  return true;
+}
+
 size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
   if (T <= 0) return 0;
   return fwd_layout(T, K, N, r).total;
@@ -127,6 +145,9 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
     if (e != hipSuccess) return e;
   }
   FwdGemmParams p{};
+  hipError_t es = hipSuccess;
+  p.status = status_word(&es);
+  if (!p.status) return es;
   p.X = X;
   p.codes = a.codes;
   p.q8 = a.q8;
@@ -213,6 +234,8 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   e = launch_tokdot2(jb, ja, a.T, TP, a.r, s);
   if (e != hipSuccess) return e;
   DxGemmParams p{};
+  p.status = status_word(&e);
+  if (!p.status) return e;
   p.dY = dY;
   p.codes = a.codes;
   p.q8 = a.q8;

@@ -10,6 +10,7 @@
 #include "../../include/qlora.h"
 #include "codebook.hpp"
 #include "common.hpp"
+#include "device_state.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -46,6 +47,7 @@ int check_linear_shape(int64_t T, int64_t K, int64_t N, int32_t r) {
   if (K % 64 != 0 || N % 8 != 0) return QLORA_ERR_SHAPE;
   if (T > (int64_t(1) << 31) || K > (int64_t(1) << 28) || N > (int64_t(1) << 28)) return QLORA_ERR_SHAPE;
   if (r < 8 || r > 128 || r % 8 != 0) return QLORA_ERR_UNSUPPORTED;
+  if (!qlora::linear_views_fit(T, K, N, r)) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 
@@ -66,11 +68,20 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported blocksize or rank";
     case QLORA_ERR_HIP: return "QLORA_ERR_HIP: a HIP call failed (see qlora_last_hip_error)";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_DEVICE:
+      return "QLORA_ERR_DEVICE: a kernel's bounded wait ran out; results since the last status query are unreliable";
     default: return "unknown qlora_status";
   }
 }
 
 int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+int qlora_device_status(void* stream) {
+  int bits = 0;
+  const int st = hip_status(qlora::take_status((hipStream_t)stream, &bits));
+  if (st != QLORA_OK) return st;
+  return bits ? QLORA_ERR_DEVICE : QLORA_OK;
+}
 
 void qlora_timing_enable(int on) { qlora::timing_enable(on != 0); }
 

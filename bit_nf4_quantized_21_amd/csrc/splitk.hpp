@@ -18,6 +18,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "device_state.hpp"
 
 namespace qlora {
 
@@ -74,9 +75,12 @@ __device__ __forceinline__ void splitk_add_slots(f32x16 (&acc)[NA][NB], rsrc_t r
 // full sum); false in the others, which must exit without storing.  Called by
 // all NT threads of the workgroup; flag is one int of LDS.  `ticket` and
 // `published` are the tile's two counts (zero on entry, left zero).
+// `status` is the device's status word: if the finisher's bounded wait ever
+// ran out, it sets kStatusSplitWait there (the sum is then incomplete and the
+// host learns of it from qlora_device_status).
 template <int NA, int NB, int NT = 256>
 __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __restrict__ slots, int* ticket,
-                                               int* published, int S, int sidx, int* flag) {
+                                               int* published, int S, int sidx, int* flag, int* status) {
   static_assert(NA * NB * 16 * NT == kSplitSlotFloats, "tile size");
   const int tid = threadIdx.x;
   const rsrc_t rs = make_rsrc(slots, (int64_t)S * kSplitSlotFloats * 4);
@@ -104,12 +108,15 @@ __device__ __forceinline__ bool splitk_combine(f32x16 (&acc)[NA][NB], float* __r
     return false;
   }
   // The others hold earlier tickets: they are past their main loops and
-  // only store and publish.  The bound is a guard that is never reached.
+  // only store and publish.  The bound is a guard that is never reached; if
+  // it were, the status word records it.
   if (tid == 0) {
-    for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= S - 1) break;
-      __builtin_amdgcn_s_sleep(2);
+    bool done = false;
+    for (int spin = 0; spin < (1 << 24) && !done; ++spin) {
+      done = __hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= S - 1;
+      if (!done) __builtin_amdgcn_s_sleep(2);
     }
+    if (!done) __hip_atomic_fetch_or(status, kStatusSplitWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   __syncthreads();
   splitk_add_slots<3, 8>(acc, rs, S, sidx);

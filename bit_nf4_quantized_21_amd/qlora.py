@@ -35,6 +35,7 @@ _SIGNATURES = {
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_last_hip_error": (ctypes.c_int, []),
+    "qlora_device_status": (ctypes.c_int, [_c_p]),
 }
 
 
@@ -83,6 +84,21 @@ def _dev(t, dtype, name):
     return t
 
 
+def _need(t, n, name):
+    """The caller's buffer must hold at least n elements (a short buffer would
+    be written past its end by the kernels)."""
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, {n} needed")
+    return t
+
+
+def _weight(codes, q8, s2, N, K):
+    nb = N * K // 64
+    _need(codes, N * K // 2, "codes")
+    _need(q8, nb, "q8")
+    _need(s2, (nb + 255) // 256, "s2")
+
+
 def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -91,6 +107,12 @@ def _stream(stream=None):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def device_status(stream=None):
+    """Raise QLoRAError if a kernel's bounded wait ran out since the last
+    query (waits for the stream; clears the status)."""
+    _check(lib().qlora_device_status(_stream(stream)))
 
 
 def timing_enable(on=True):
@@ -166,6 +188,10 @@ def dequantize_nf4(codes, q8, s2, n, dtype=None, out=None, stream=None):
     _dev(s2, torch.float32, "s2")
     out = torch.empty(n, dtype=dtype, device=codes.device) if out is None else out
     _dev(out, dtype, "out")
+    _need(codes, n // 2, "codes")
+    _need(q8, (n + 63) // 64, "q8")
+    _need(s2, ((n + 63) // 64 + 255) // 256, "s2")
+    _need(out, n, "out")
     _check(lib().qlora_dequantize_nf4(_p(codes), _p(q8), _p(s2), n, 1 if dtype == torch.bfloat16 else 0,
                                       _p(out), _stream(stream)))
     return out
@@ -180,12 +206,17 @@ def linear_bwd_workspace_bytes(T, K, N, r):
 
 
 def _workspace(nbytes, device, ws):
+    """The caller's workspace if given (the library checks its size), else a
+    new one of the size the library asks for."""
     torch = _torch()
-    if nbytes == 0:
+    if ws is not None:
+        _dev(ws, torch.uint8, "workspace")
+        if ws.numel() < nbytes:
+            raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
         return ws
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return ws
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None, stream=None):
@@ -201,10 +232,11 @@ def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None
     r = A.shape[1]
     if A.shape != (K, r) or B.shape != (r, N):
         raise ValueError("A must be [K,r] and B [r,N]")
+    _weight(codes, q8, s2, N, K)
     Y = torch.empty(T, N, dtype=torch.bfloat16, device=X.device) if Y is None else Y
     XA = torch.empty(T, r, dtype=torch.float32, device=X.device) if XA is None else XA
-    _dev(Y, torch.bfloat16, "Y")
-    _dev(XA, torch.float32, "XA")
+    _need(_dev(Y, torch.bfloat16, "Y"), T * N, "Y")
+    _need(_dev(XA, torch.float32, "XA"), T * r, "XA")
     nbytes = linear_fwd_workspace_bytes(T, K, N, r)
     workspace = _workspace(nbytes, X.device, workspace)
     _check(lib().qlora_linear_fwd(_p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r, float(alpha),
@@ -228,11 +260,12 @@ def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None,
     r = A.shape[1]
     if A.shape != (K, r) or B.shape != (r, N) or dY.shape[0] != T or XA.shape != (T, r):
         raise ValueError("shape mismatch")
+    _weight(codes, q8, s2, N, K)
     dX = torch.empty(T, K, dtype=torch.bfloat16, device=X.device) if dX is None else dX
     dA = torch.empty(K, r, dtype=torch.bfloat16, device=X.device) if dA is None else dA
     dB = torch.empty(r, N, dtype=torch.bfloat16, device=X.device) if dB is None else dB
-    for t, nm in ((dX, "dX"), (dA, "dA"), (dB, "dB")):
-        _dev(t, torch.bfloat16, nm)
+    for t, nm, n in ((dX, "dX", T * K), (dA, "dA", K * r), (dB, "dB", r * N)):
+        _need(_dev(t, torch.bfloat16, nm), n, nm)
     nbytes = linear_bwd_workspace_bytes(T, K, N, r)
     workspace = _workspace(nbytes, X.device, workspace)
     _check(lib().qlora_linear_bwd(_p(dY), _p(X), _p(XA), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r,

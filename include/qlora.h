@@ -52,7 +52,8 @@ typedef enum {
   QLORA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
   QLORA_ERR_UNSUPPORTED = -4, /* blocksize != 64 / 256, rank outside [8,128] or not a multiple of 8 */
   QLORA_ERR_HIP = -5,         /* a HIP launch or query failed; see qlora_last_hip_error() */
-  QLORA_ERR_WORKSPACE = -6    /* workspace NULL or smaller than the *_workspace_bytes query */
+  QLORA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  QLORA_ERR_DEVICE = -7       /* a kernel's bounded wait ran out (reported by qlora_device_status) */
 } qlora_status;
 
 /*
@@ -119,6 +120,20 @@ int qlora_double_quant(const float* absmax, int64_t nb, int32_t blocksize2,
  *   K            in_features: K >= 64, K % 64 == 0.
  *   N            out_features: N >= 8, N % 8 == 0.
  *   r            LoRA rank: 8 <= r <= 128, r % 8 == 0.
+ *   Size limits: every kernel addresses its operands through 32-bit buffer
+ *   views, so N*K/2, T*K*2 and T*N*2 bytes (and each internal workspace
+ *   region) must each be below 2^31; larger problems return
+ *   QLORA_ERR_SHAPE before anything is enqueued (split them along T or N).
+ *   Why the rank is narrowed: the kernels move rank-r rows of A, B, XA and
+ *   the gradients as 16-byte vectors of 8 values and keep up to 128 fp32
+ *   rank columns per lane group in registers.  Ranks that are multiples of
+ *   8 up to 128 cover the usual LoRA ranks (8 ... 128).  Another rank r' is
+ *   served by padding: pass A with zero columns and B with zero rows up to
+ *   r = the next multiple of 8, and alpha * r / r' as alpha so that alpha / r
+ *   is the intended alpha / r' (up to one rounding of alpha; exact when both
+ *   are powers of two); Y, XA's first r' columns, dX and the first r'
+ *   columns/rows of dA/dB are then those of rank r', the padding's are zero.
+ *   Why N % 8: rows of Y and dB are stored as 16-byte vectors.
  *   Y     [T,N]  out: bf16.
  *   XA    [T,r]  out: fp32.
  *   workspace    device scratch of at least
@@ -187,6 +202,18 @@ const char* qlora_status_string(int status);
 
 /* Host: the HIP error code behind the last QLORA_ERR_HIP on this thread. */
 int qlora_last_hip_error(void);
+
+/*
+ * Support: the device status of the current GPU.  The split-contraction
+ * hand-off of the dequant-GEMMs waits a bounded time for the other slices of
+ * a tile (a guard that is never reached when every slice runs); if the
+ * bound ever ran out, the finishing workgroup sets a status bit on the
+ * device and stores an incomplete sum.  This call waits for `stream`,
+ * returns QLORA_ERR_DEVICE if any bit is set (the outputs of the calls since
+ * the previous query are then unreliable) and clears the bits; QLORA_OK
+ * otherwise, or QLORA_ERR_HIP if the wait or the read failed.  Host-blocking.
+ */
+int qlora_device_status(void* stream);
 
 #ifdef __cplusplus
 }

@@ -113,3 +113,34 @@ def test_linear_bwd_argument_errors(L):
     need = L.qlora_linear_bwd_workspace_bytes(2048, 4096, 11008, 64)
     if need:
         assert bwd(T=2048, K=4096, N=11008, r=64, wsb=need - 1) == EWS
+
+
+def test_views_beyond_31_bits_are_refused(L):
+    """Operands or workspace regions that would not fit the kernels' 32-bit
+    buffer views are refused on the host instead of being read as zeros."""
+    assert _fwd(L, T=4, K=65536, N=65536, r=8) == ESHAPE         # codes: N*K/2 = 2^31 bytes
+    assert _fwd(L, T=1 << 24, K=64, N=64, r=8) == ESHAPE          # X: T*K*2 = 2^31 bytes
+    assert _fwd(L, T=(1 << 24) - 8, K=64, N=128, r=8) == ESHAPE  # Y: T*N*2 > 2^31 bytes
+    assert L.qlora_linear_fwd_workspace_bytes(1 << 24, 64, 64, 8) == 0
+    assert L.qlora_linear_bwd_workspace_bytes(4, 65536, 65536, 8) == 0
+    # the largest configured layers are accepted
+    for (T, K, N) in ((512, 8192, 22016), (512, 22016, 8192), (4096, 17920, 6656), (2048, 11008, 4096)):
+        assert L.qlora_linear_fwd_workspace_bytes(T, K, N, 64) > 0
+        assert L.qlora_linear_bwd_workspace_bytes(T, K, N, 64) > 0
+
+
+def test_device_status_is_exported_and_documented(L):
+    assert hasattr(L, "qlora_device_status")
+    assert L.qlora_status_string(-7).startswith(b"QLORA_ERR_DEVICE")
+
+
+def test_binding_checks_buffer_sizes():
+    """The binding refuses caller buffers shorter than the call writes."""
+    torch = pytest.importorskip("torch")
+    t = torch.empty(10)
+    assert qlora._need(t, 10, "t") is t
+    with pytest.raises(ValueError):
+        qlora._need(t, 11, "t")
+    with pytest.raises(ValueError):
+        qlora._weight(torch.empty(10, dtype=torch.uint8), torch.empty(1, dtype=torch.uint8),
+                      torch.empty(1), 8, 64)
