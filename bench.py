@@ -1,33 +1,45 @@
 #!/usr/bin/env python3
 """Benchmark of the QLoRA NF4 linear hot path on one MI355X.
 
-Step (the timed unit): forward + backward of every linear of the workload
-(default: the LLaMA-7B MLP, gate/up 4096->11008 and down 11008->4096, 2048
-tokens, LoRA r=64, alpha=16), on synthetic seeded inputs already resident in
-HBM.  `value` is the algorithmic fwd+bwd rate, sum over linears of
+Headline (the `value` of the JSON line): the LLaMA-65B-shaped full weight set,
+80 layers x (q, k, v, o, gate, up, down) = 560 frozen NF4 + double-quant
+linears resident in HBM (hidden 8192, MLP 22016), each with a rank-64 LoRA
+adapter (alpha 16).  A step is the forward of all 560 linears in layer order
+followed by the backward of all 560 in reverse order, at 512 tokens, every
+linear on its own seeded synthetic input (nothing between the linears).
+`value` is the algorithmic fwd+bwd rate, sum over linears of
 4 T N K + 6 T r (K + N) flop per step, divided by the host wall time of
-exactly --steps steps bracketed by device synchronisations.
+exactly --steps steps bracketed by device synchronisations.  Before the steps
+the whole set is quantized on the device ("quantize_all": fp32 weights drawn
+per layer, 3.2 GB a layer, every launch reading cold HBM), which is timed by
+HIP events around the quantization kernels alone.
 
 Beside it, in the same JSON line:
-  roofline      the dominant kernel's algorithmic rate against the MI355X peak,
-                from HIP events recorded on its launch stream during the timed
-                steps (the library's per-kernel timing hooks);
-  gemv          the small-token forward (LLaMA-7B q_proj 4096x4096, 4 tokens,
-                r=64): dequant-GEMV kernel GB/s over 40 rotating weight copies
-                (> 256 MB, so every launch streams the 4-bit weights from HBM);
-  quantize      blockwise NF4 quantization (fp32 and bf16 weights) + double
-                quantization GB/s;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+  roofline      the dominant kernel's algorithmic rate against the MI355X
+                peak, from HIP events recorded on its launch stream during a
+                second pass of the same steps;
+  workloads     the LLaMA-33B decoder-layer linears (T=4096) and the
+                LLaMA-7B MLP (T=2048), each with its own rate and roofline;
+  gemv          the small-token forward (4096x4096, 4 tokens, r=64) over 48
+                rotating weight copies (> 390 MB of codes: cold HBM);
+  quantize      11008x4096 weights (fp32 and bf16) over 40 rotating source
+                copies, median per-launch event time;
+  peaks         the copy and bf16-MFMA rates this GPU sustains (probes), with
+                the headline fractions against them;
+  cpu_baseline  the CPU oracle on a bounded sample, per stage, median of 3.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp7b|layer33b|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload full65b|layer33b|mlp7b|tiny]
+                    [--no-extras] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,10 +49,6 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # HBM3E
 METRIC = "QLoRA NF4 linear fwd+bwd TFLOP/s and dequant-GEMV GB/s, % of MI355X roofline"
-
-
-def fwd_flops(T, N, K, r):
-    return 2 * T * N * K + 2 * T * r * (K + N)
 
 
 def fwdbwd_flops(T, N, K, r):
@@ -56,11 +64,15 @@ def kernel_flops(name, T, N, K, r):
     return None
 
 
+def dq_bytes(N, K):
+    nb = N * K // 64
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256)
+
+
 def gemv_kernel_bytes(T, N, K, r):
     """Algorithmic HBM bytes of one dequant-GEMV launch: codes, 8-bit and
     fp32 second-level constants, X, B, XA in and Y out, each once."""
-    nb = N * K // 64
-    return N * K // 2 + nb + 4 * ((nb + 255) // 256) + 2 * T * K + 2 * r * N + 4 * T * r + 2 * T * N
+    return dq_bytes(N, K) + 2 * T * K + 2 * r * N + 4 * T * r + 2 * T * N
 
 
 def gemv_path_bytes(T, N, K, r):
@@ -89,22 +101,96 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def make_layer(torch, qlora, synth, T, N, K, r, i, backward=True):
-    inp = synth.device_inputs(T, N, K, r, i, backward=backward)
-    codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
-    q8, s2 = qlora.double_quant(absmax)
-    del inp["W"], absmax
-    L = dict(T=T, N=N, K=K, r=r, codes=codes, q8=q8, s2=s2, **inp)
-    dev = codes.device
-    L["Y"] = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
-    L["XA"] = torch.empty(T, r, dtype=torch.float32, device=dev)
-    L["wsf"] = torch.empty(max(1, qlora.linear_fwd_workspace_bytes(T, K, N, r)), dtype=torch.uint8, device=dev)
-    if backward:
-        L["dX"] = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
-        L["dA"] = torch.empty(K, r, dtype=torch.bfloat16, device=dev)
-        L["dB"] = torch.empty(r, N, dtype=torch.bfloat16, device=dev)
-        L["wsb"] = torch.empty(max(1, qlora.linear_bwd_workspace_bytes(T, K, N, r)), dtype=torch.uint8, device=dev)
-    return L
+def median(xs):
+    return statistics.median(xs)
+
+
+# ---------------------------------------------------------------------------
+# Workload set-up: quantized weights resident in HBM plus per-linear inputs.
+# ---------------------------------------------------------------------------
+def linear_list(wl):
+    """(seed index, name, N, K) of every linear of the workload, layer-major."""
+    out = []
+    for layer in range(wl.layers):
+        for j, lin in enumerate(wl.linears):
+            out.append((layer * len(wl.linears) + j, lin.name, lin.N, lin.K))
+    return out
+
+
+def quantize_all(torch, qlora, synth, wl, lins):
+    """Quantize every linear of the workload from fp32 weights drawn on the
+    device one layer at a time (one layer's fp32 set is generated, then its
+    linears are quantized in generation order, so each read is from cold
+    HBM), and time the quantization kernels with HIP events."""
+    per_layer = len(wl.linears)
+    layer_elems = sum(l.N * l.K for l in wl.linears)
+    buf = torch.empty(layer_elems, dtype=torch.float32, device="cuda")
+    max_nb = max(l.N * l.K // 64 for l in wl.linears)
+    absmax = torch.empty(max_nb, dtype=torch.float32, device="cuda")
+    weights = []
+    qlora.timing_read()
+    for layer in range(wl.layers):
+        chunk = lins[layer * per_layer:(layer + 1) * per_layer]
+        views, off = [], 0
+        for (i, _, N, K) in chunk:
+            v = buf[off:off + N * K]
+            synth.device_weight(v, i)
+            views.append(v)
+            off += N * K
+        qlora.timing_enable(True)
+        for (i, _, N, K), v in zip(chunk, views):
+            n = N * K
+            codes = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
+            q8 = torch.empty(n // 64, dtype=torch.uint8, device="cuda")
+            s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device="cuda")
+            qlora.quantize_nf4(v, codes, absmax[: n // 64])
+            qlora.double_quant(absmax[: n // 64], q8, s2)
+            weights.append((codes, q8, s2))
+        qlora.timing_enable(False)
+    torch.cuda.synchronize()
+    kt = qlora.timing_read()
+    del buf, absmax
+    torch.cuda.empty_cache()
+    params = sum(N * K for (_, _, N, K) in lins)
+    ms = sum(t for (_, t) in kt.values())
+    # algorithmic bytes: fp32 weights read once; codes, absmax written and
+    # absmax read back by the double quantization; q8 and s2 written
+    nb = params // 64
+    alg = 4 * params + params // 2 + 4 * nb + 4 * nb + nb + 4 * ((nb + 255) // 256)
+    res = {"workload": f"{wl.name}: quantize all {len(lins)} linears from fp32 (blockwise NF4 + double quant)",
+           "params": params, "kernel_ms": round(ms, 3),
+           "kernels": {k: {"launches": n, "total_ms": round(t, 3)} for k, (n, t) in kt.items()},
+           "algorithmic_bytes": alg, "GBs": round(alg / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "note": "fp32 source drawn on the device per layer (3.2 GB) and never resident as a whole; "
+                   "only the quantization kernels are timed"}
+    return weights, res
+
+
+def make_linears(torch, qlora, synth, wl, lins, weights):
+    """Per-linear inputs and gradients; shared Y / dX outputs and workspaces."""
+    T, r = wl.T, wl.r
+    Ls = []
+    for (i, name, N, K), (codes, q8, s2) in zip(lins, weights):
+        inp = synth.device_inputs(T, N, K, r, i, backward=True, weight=False)
+        L = dict(T=T, N=N, K=K, r=r, codes=codes, q8=q8, s2=s2, **inp)
+        L["XA"] = torch.empty(T, r, dtype=torch.float32, device="cuda")
+        L["dA"] = torch.empty(K, r, dtype=torch.bfloat16, device="cuda")
+        L["dB"] = torch.empty(r, N, dtype=torch.bfloat16, device="cuda")
+        Ls.append(L)
+    maxN = max(L["N"] for L in Ls)
+    maxK = max(L["K"] for L in Ls)
+    Ybuf = torch.empty(T * maxN, dtype=torch.bfloat16, device="cuda")
+    dXbuf = torch.empty(T * maxK, dtype=torch.bfloat16, device="cuda")
+    wsf = max(qlora.linear_fwd_workspace_bytes(T, L["K"], L["N"], r) for L in Ls)
+    wsb = max(qlora.linear_bwd_workspace_bytes(T, L["K"], L["N"], r) for L in Ls)
+    wsf = torch.empty(max(1, wsf), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(1, wsb), dtype=torch.uint8, device="cuda")
+    for L in Ls:
+        L["Y"] = Ybuf[: T * L["N"]].view(T, L["N"])
+        L["dX"] = dXbuf[: T * L["K"]].view(T, L["K"])
+        L["wsf"], L["wsb"] = wsf, wsb
+    return Ls
 
 
 def run_fwd(qlora, L, alpha):
@@ -117,78 +203,110 @@ def run_bwd(qlora, L, alpha):
                      dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
 
 
-def bench_step(torch, qlora, synth, wl, steps, warmup):
-    layers = [make_layer(torch, qlora, synth, wl.T, lin.N, lin.K, wl.r, i) for i, lin in enumerate(wl.linears)]
+def time_steps(torch, qlora, wl, Ls, steps, warmup, event_steps):
+    """Wall time per step of the fwd (layer order) + bwd (reverse order) step,
+    then per-kernel event times from a second pass of event_steps steps."""
+    alpha = wl.alpha
 
     def step():
-        for L in layers:
-            run_fwd(qlora, L, wl.alpha)
-            run_bwd(qlora, L, wl.alpha)
+        for L in Ls:
+            run_fwd(qlora, L, alpha)
+        for L in reversed(Ls):
+            run_bwd(qlora, L, alpha)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # Throughput: K steps with no instrumentation in the stream.
+    qlora.device_status()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / steps
-    # Per-kernel durations: the same K steps again with a HIP event pair
-    # recorded around every launch, on the stream it is launched on (the
-    # events add a few microseconds between kernels, so this pass does not
-    # give the throughput).
+    # second pass: every library kernel bracketed by events on its stream
     qlora.timing_read()
     qlora.timing_enable(True)
-    torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(event_steps):
         step()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     qlora.timing_enable(False)
     kt = qlora.timing_read()
-    ms_timed = (t3 - t2) * 1e3 / steps
-    flops = sum(fwdbwd_flops(L["T"], L["N"], L["K"], L["r"]) for L in layers)
-    # dominant kernel: largest total time in the timed steps
-    dom = max(kt.items(), key=lambda kv: kv[1][1])
-    name, (launches, total_ms) = dom
-    per_step_flops = [kernel_flops(name, L["T"], L["N"], L["K"], L["r"]) for L in layers]
+    qlora.device_status()   # raises if a split hand-off wait ever ran out
+    flops = sum(fwdbwd_flops(L["T"], L["N"], L["K"], L["r"]) for L in Ls)
+    name, (launches, total_ms) = max(kt.items(), key=lambda kv: kv[1][1])
+    per_step = [kernel_flops(name, L["T"], L["N"], L["K"], L["r"]) for L in Ls]
     roof = None
-    if all(f is not None for f in per_step_flops):
-        alg = sum(per_step_flops) * steps
-        achieved = alg / (total_ms * 1e-3) / 1e12
+    if all(f is not None for f in per_step):
+        achieved = sum(per_step) * event_steps / (total_ms * 1e-3) / 1e12
         roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_profiles(name, "mlp7b"),
-                "avg_launch_us": round(total_ms * 1e3 / launches, 2), "launches": launches}
-    kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 2), "share": round(t / sum(v[1] for v in kt.values()), 4)}
+                "traffic": traffic_from_profiles(name, WORKLOAD_TAG.get(wl.name, wl.name)),
+                "avg_launch_us": round(total_ms * 1e3 / launches, 2), "launches": launches,
+                "algorithmic_flop_per_launch": round(sum(per_step) / len(per_step)),
+                "events_pass_ms_per_step": round((t3 - t2) * 1e3 / event_steps, 4)}
+    tot = sum(v[1] for v in kt.values())
+    kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 2), "share": round(t / tot, 4)}
                for k, (n, t) in sorted(kt.items(), key=lambda kv: -kv[1][1])}
-    if roof is not None:
-        roof["events_pass_ms_per_step"] = round(ms_timed, 4)
-    del layers
-    torch.cuda.empty_cache()
     return ms, flops, roof, kernels
 
 
-def bench_gemv(torch, qlora, synth, copies=40, iters=200):
+WORKLOAD_TAG = {"llama65b-80layers-T512-r64": "full65b", "llama33b-layer-T4096-r64": "layer33b",
+                "llama7b-mlp-T2048-r64": "mlp7b", "tiny-512x512-T32-r8": "tiny"}
+
+
+def bench_workload(torch, qlora, synth, key, steps, warmup, event_steps=2):
+    wl = synth.WORKLOADS[key]
+    lins = linear_list(wl)
+    weights, qres = quantize_all(torch, qlora, synth, wl, lins)
+    Ls = make_linears(torch, qlora, synth, wl, lins, weights)
+    del weights
+    ms, flops, roof, kernels = time_steps(torch, qlora, wl, Ls, steps, warmup, event_steps)
+    value = flops / (ms * 1e-3) / 1e12
+    res = {"workload": wl.name, "tokens": wl.T, "r": wl.r, "alpha": wl.alpha, "layers": wl.layers,
+           "linears": [[l.name, l.N, l.K] for l in wl.linears], "flop_per_step": flops,
+           "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
+           "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4), "roofline": roof, "kernels": kernels,
+           "quantize_all": qres}
+    del Ls
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Small-token forward (dequant-GEMV) and quantization throughput, cold HBM.
+# ---------------------------------------------------------------------------
+def bench_gemv(torch, qlora, synth, copies=48, iters=240):
     T, N, K, r, alpha = 4, 4096, 4096, 64, 16.0
-    layers = [make_layer(torch, qlora, synth, T, N, K, r, i, backward=False) for i in range(copies)]
-    X = layers[0]["X"]
-    for L in layers:
-        L["X"] = X
+    lins = [(i, "q_proj", N, K) for i in range(copies)]
+    Ls = []
+    for (i, _, n_, k_) in lins:
+        inp = synth.device_inputs(T, n_, k_, r, i, backward=False)
+        codes, absmax = qlora.quantize_nf4(inp.pop("W").view(-1))
+        q8, s2 = qlora.double_quant(absmax)
+        L = dict(T=T, N=N, K=K, r=r, codes=codes, q8=q8, s2=s2, **inp)
+        Ls.append(L)
+    X = Ls[0]["X"]
+    Y = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    XA = torch.empty(T, r, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, qlora.linear_fwd_workspace_bytes(T, K, N, r)), dtype=torch.uint8, device="cuda")
+    for L in Ls:
+        L.update(X=X, Y=Y, XA=XA, wsf=ws)
     for i in range(2 * copies):
-        run_fwd(qlora, layers[i % copies], alpha)
-    torch.cuda.synchronize()
-    qlora.timing_read()
-    qlora.timing_enable(True)
+        run_fwd(qlora, Ls[i % copies], alpha)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(iters):
-        run_fwd(qlora, layers[i % copies], alpha)
+        run_fwd(qlora, Ls[i % copies], alpha)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    qlora.timing_read()
+    qlora.timing_enable(True)
+    for i in range(iters):
+        run_fwd(qlora, Ls[i % copies], alpha)
+    torch.cuda.synchronize()
     qlora.timing_enable(False)
     kt = qlora.timing_read()
     n, total = kt["gemv_fwd_kernel"]
@@ -196,126 +314,188 @@ def bench_gemv(torch, qlora, synth, copies=40, iters=200):
     kb = gemv_kernel_bytes(T, N, K, r)
     gbs = kb / (us * 1e-6) / 1e9
     fwd_us = sum(t for (_, t) in kt.values()) * 1e3 / iters
-    wall_us = (t1 - t0) * 1e6 / iters
     res = {"workload": "llama7b-q_proj-gemv-T4-r64 (4096x4096 NF4+DQ, 4 tokens, fwd)",
            "value": round(gbs, 1), "unit": "GB/s",
            "roofline": {"kernel": "gemv_fwd_kernel", "bound": "hbm", "achieved": round(gbs, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profiles("gemv_fwd_kernel", "gemv7b"),
                         "avg_launch_us": round(us, 3), "bytes_per_launch": kb},
-           "fwd_path_us_gpu": round(fwd_us, 3), "fwd_path_GBs_gpu": round(gemv_path_bytes(T, N, K, r) / (fwd_us * 1e-6) / 1e9, 1),
-           "fwd_call_us_wall": round(wall_us, 3),
+           "fwd_path_us_gpu": round(fwd_us, 3),
+           "fwd_path_GBs_gpu": round(gemv_path_bytes(T, N, K, r) / (fwd_us * 1e-6) / 1e9, 1),
+           "fwd_call_us_wall": round((t1 - t0) * 1e6 / iters, 3),
            "kernels_avg_us": {k: round(t * 1e3 / c, 3) for k, (c, t) in kt.items()},
-           "weight_copies": copies}
-    del layers
+           "weight_copies": copies, "codes_bytes_rotated": copies * dq_bytes(N, K)}
+    del Ls
     torch.cuda.empty_cache()
     return res
 
 
-def bench_quantize(torch, qlora, iters=10):
+def _event_median(torch, fn, items, reps):
+    """Median over reps calls of fn(item) (items rotated) of the per-call
+    event time on the current stream, in microseconds."""
+    times = []
+    s = torch.cuda.current_stream()
+    for k in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn(items[k % len(items)])
+        b.record(s)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    return median([a.elapsed_time(b) * 1e3 for (a, b) in times])
+
+
+def bench_quantize(torch, qlora, copies=40, reps=80):
+    """Quantization of 11008 x 4096 weights, 40 distinct source copies (7.2 GB
+    fp32, 3.6 GB bf16) rotated so every launch reads cold HBM; median of the
+    per-launch event times."""
     N, K = 11008, 4096
     n = N * K
-    srcs = []
-    for i in range(2):
-        g = torch.Generator(device="cuda")
-        g.manual_seed(1000 + i)
-        srcs.append(torch.randn(n, generator=g, device="cuda", dtype=torch.float32) * 0.02)
+    nb = n // 64
     codes = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
-    absmax = torch.empty(n // 64, dtype=torch.float32, device="cuda")
-    q8 = torch.empty(n // 64, dtype=torch.uint8, device="cuda")
-    s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device="cuda")
-    for i in range(4):
-        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
-        qlora.double_quant(absmax, q8, s2)
-    torch.cuda.synchronize()
-    qlora.timing_read()
-    qlora.timing_enable(True)
-    for i in range(iters):
-        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
-        qlora.double_quant(absmax, q8, s2)
-    torch.cuda.synchronize()
-    qlora.timing_enable(False)
-    kt = qlora.timing_read()
-    qn, qt = kt["quantize_nf4_kernel"]
-    dn, dt = kt["double_quant_kernel"]
-    qbytes = 4 * n + n // 2 + 4 * (n // 64)
-    dbytes = 4 * (n // 64) + n // 64 + 4 * ((n // 64 + 255) // 256)
-    q_us, d_us = qt * 1e3 / qn, dt * 1e3 / dn
-    res = {"workload": "quantize 11008x4096 fp32 -> NF4 + double quant",
-           "quantize": {"avg_us": round(q_us, 2), "GBs": round(qbytes / (q_us * 1e-6) / 1e9, 1),
-                        "frac_hbm": round(qbytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": qbytes},
-           "double_quant": {"avg_us": round(d_us, 2), "GBs": round(dbytes / (d_us * 1e-6) / 1e9, 1), "bytes": dbytes}}
-    # The same weights stored as bf16 (how pretrained checkpoints ship).
+    absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+    q8 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device="cuda")
+    from bit_nf4_quantized_21_amd import synth
+    srcs = [synth.device_weight(torch.empty(n, dtype=torch.float32, device="cuda"), i) for i in range(copies)]
+    absmaxes = [qlora.quantize_nf4(x, codes)[1] for x in srcs[:8]]
+    for x in srcs:
+        qlora.quantize_nf4(x, codes, absmax)
+    q_us = _event_median(torch, lambda x: qlora.quantize_nf4(x, codes, absmax), srcs, reps)
+    d_us = _event_median(torch, lambda a: qlora.double_quant(a, q8, s2), absmaxes, reps)
+    qbytes = 4 * n + n // 2 + 4 * nb
+    dbytes = 4 * nb + nb + 4 * ((nb + 255) // 256)
+    res = {"workload": "quantize 11008x4096 -> NF4 + double quant, 40 rotating source copies",
+           "source_bytes_rotated": copies * 4 * n,
+           "quantize_fp32": {"median_us": round(q_us, 2), "GBs": round(qbytes / (q_us * 1e-6) / 1e9, 1),
+                             "frac_hbm": round(qbytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": qbytes},
+           "double_quant": {"median_us": round(d_us, 2), "GBs": round(dbytes / (d_us * 1e-6) / 1e9, 1),
+                            "bytes": dbytes, "note": "absmax input of 2.8 MB (a warm-cache size by nature)"}}
     srcs = [x.to(torch.bfloat16) for x in srcs]
-    for i in range(4):
-        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
-    torch.cuda.synchronize()
-    qlora.timing_read()
-    qlora.timing_enable(True)
-    for i in range(iters):
-        qlora.quantize_nf4(srcs[i % 2], codes, absmax)
-    torch.cuda.synchronize()
-    qlora.timing_enable(False)
-    bn, bt = qlora.timing_read()["quantize_nf4_bf16_kernel"]
-    bbytes = 2 * n + n // 2 + 4 * (n // 64)
-    b_us = bt * 1e3 / bn
-    res["quantize_bf16"] = {"avg_us": round(b_us, 2), "GBs": round(bbytes / (b_us * 1e-6) / 1e9, 1),
+    torch.cuda.empty_cache()
+    for x in srcs:
+        qlora.quantize_nf4(x, codes, absmax)
+    b_us = _event_median(torch, lambda x: qlora.quantize_nf4(x, codes, absmax), srcs, reps)
+    bbytes = 2 * n + n // 2 + 4 * nb
+    res["quantize_bf16"] = {"median_us": round(b_us, 2), "GBs": round(bbytes / (b_us * 1e-6) / 1e9, 1),
                             "frac_hbm": round(bbytes / (b_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": bbytes}
     del srcs
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(synth, T_sample=2048, budget_s=30.0):
-    """The oracle, untuned, on the bench step itself: the three 7B MLP linears
-    (gate, up, down) at T_sample tokens, r=64, each as fp64 dequantize +
-    forward + backward. Quantization of W happens before the timed region.
-    Linears are taken in order and the sample stops early once budget_s of
-    CPU time has been spent, so a slow host still finishes in bounded time."""
+def measure_peaks(torch):
+    """The copy bandwidth and bf16 MFMA rate this GPU sustains (probes in
+    bench_peaks.so), medians of 5 event-timed launches."""
+    path = os.path.join(ROOT, "bench_peaks.so")
+    if not os.path.exists(path):
+        return None
+    P = ctypes.CDLL(path)
+    P.qlora_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.qlora_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    blocks, iters = 1024, 20000
+    for _ in range(2):
+        P.qlora_peak_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), st)
+    us = _event_median(torch, lambda _: P.qlora_peak_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), st),
+                       [0], 5)
+    mfma = blocks * 4 * iters * 8 * 32 * 32 * 16 * 2 / (us * 1e-6) / 1e12
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        P.qlora_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 8192, st)
+    cus = _event_median(torch, lambda _: P.qlora_peak_copy(ctypes.c_void_p(src.data_ptr()),
+                                                            ctypes.c_void_p(dst.data_ptr()), nbytes, 8192, st),
+                        [0], 5)
+    copy = 2 * nbytes / (cus * 1e-6) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_TFLOPs": round(mfma, 1), "mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
+            "copy_GBs": round(copy, 1), "copy_frac_of_spec": round(copy / PEAK_HBM_GBS, 4),
+            "probes": "v_mfma_f32_32x32x16_bf16 chains, 4 waves per SIMD; 2 GiB device copy (read + write)"}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untouched, on a bounded sample.
+# ---------------------------------------------------------------------------
+def cpu_baseline(synth):
+    """The oracle timed per stage on one linear of the 65B set (q_proj,
+    8192 x 8192, 512 tokens, r=64): quantize + double quant of a 2048-row
+    slice of its weight, fp64 dequantize, forward, backward; median of 3 each.
+    The whole-set figures are extrapolated by flops and parameter count."""
+    import numpy as np
     from oracle import lora, nf4
-    r, alpha = 64, 16.0
-    done, fl, dt = [], 0.0, 0.0
-    for i, (name, N, K) in enumerate((("gate_proj", 11008, 4096), ("up_proj", 11008, 4096),
-                                      ("down_proj", 4096, 11008))):
-        W = synth.weight(N, K, i)
-        X = nf4.bf16_bits_to_f32(synth.x_bits(T_sample, K, i))
-        A = nf4.bf16_bits_to_f32(synth.a_bits(K, r, i))
-        B = nf4.bf16_bits_to_f32(synth.b_bits(r, N, i))
-        dY = nf4.bf16_bits_to_f32(synth.dy_bits(T_sample, N, i))
-        codes, q8, s2, _ = nf4.quantize_all(W)
-        del W
-        t0 = time.perf_counter()
-        Wd = nf4.dequantize(codes, q8, s2, N * K, "bf16").reshape(N, K)
-        lora.linear_fwd(X, Wd, A, B, alpha, r)
-        lora.linear_bwd(dY, X, Wd, A, B, alpha, r)
-        dt += time.perf_counter() - t0
-        fl += fwdbwd_flops(T_sample, N, K, r)
-        done.append(name)
-        del Wd, X, dY
-        if dt > budget_s:
-            break
-    cores = len(os.sched_getaffinity(0))
-    threads = cores
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    blas = cores
+    if threadpool_info is not None:
         info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
         if info:
-            threads = max(p.get("num_threads", cores) for p in info)
-    except Exception:
-        pass
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{'+'.join(done)} of the 7B MLP at {T_sample} tokens, r=64: "
-                      f"fp64 dequantize + fwd + bwd, {dt:.2f} s",
-            "host_cpus": cores}
+            blas = max(p.get("num_threads", cores) for p in info)
+    T, N, K, r, alpha = 512, 8192, 8192, 64, 16.0
+    rows = 2048
+    W = synth.weight(N, K, 0)
+    Wq = W[:rows]
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return median(ts)
+
+    t_quant = med3(lambda: nf4.quantize_nf4(Wq))
+    codes, absmax = nf4.quantize_nf4(Wq)
+    t_dq = med3(lambda: nf4.double_quant(absmax))
+    t_quant_1t = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t_quant_1t = med3(lambda: nf4.quantize_nf4(Wq))
+    codes, q8, s2, _ = nf4.quantize_all(W)
+    del W
+    t_deq = med3(lambda: nf4.dequantize(codes, q8, s2, N * K, "bf16"))
+    Wd = nf4.dequantize(codes, q8, s2, N * K, "bf16").reshape(N, K)
+    X = nf4.bf16_bits_to_f32(synth.x_bits(T, K, 0))
+    A = nf4.bf16_bits_to_f32(synth.a_bits(K, r, 0))
+    B = nf4.bf16_bits_to_f32(synth.b_bits(r, N, 0))
+    dY = nf4.bf16_bits_to_f32(synth.dy_bits(T, N, 0))
+    t_fwd = med3(lambda: lora.linear_fwd(X, Wd, A, B, alpha, r))
+    t_bwd = med3(lambda: lora.linear_bwd(dY, X, Wd, A, B, alpha, r))
+    fl = fwdbwd_flops(T, N, K, r)
+    value = fl / (t_fwd + t_bwd) / 1e12
+    qparams = rows * K
+    wl = synth.WORKLOADS["full65b"]
+    set_flops = sum(fwdbwd_flops(wl.T, l.N, l.K, wl.r) for l in wl.linears) * wl.layers
+    set_params = sum(l.N * l.K for l in wl.linears) * wl.layers
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"one 65B q_proj linear (8192x8192, T=512, r=64): fp64 forward + backward, median of 3; "
+                      f"quantize + double quant on a {rows}x{K} slice",
+            "host_cpus": cores, "blas_threads": int(blas),
+            "stages_s": {"quantize": round(t_quant, 4), "quantize_1thread": None if t_quant_1t is None
+                         else round(t_quant_1t, 4), "double_quant": round(t_dq, 4),
+                         "dequantize_fp64": round(t_deq, 4), "forward": round(t_fwd, 4),
+                         "backward": round(t_bwd, 4)},
+            "quantize_GBs": round(4.5625 * qparams / t_quant / 1e9, 4),
+            "quantize_GBs_1thread": None if t_quant_1t is None else round(4.5625 * qparams / t_quant_1t / 1e9, 4),
+            "extrapolated_full65b": {"fwd_bwd_s_per_step": round(set_flops / (value * 1e12), 1),
+                                     "quantize_all_s": round(set_params / qparams * (t_quant + t_dq), 1),
+                                     "label": "extrapolated from the one-linear sample by flops and parameters"}}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mlp7b", choices=["mlp7b", "layer33b", "tiny"])
-    ap.add_argument("--no-extras", action="store_true", help="skip the GEMV and quantize measurements")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="full65b", choices=["full65b", "layer33b", "mlp7b", "tiny"])
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline workload only (no other workloads, GEMV, quantize or peak probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -328,26 +508,48 @@ def main():
     from bit_nf4_quantized_21_amd import qlora, synth
     qlora.lib()
     torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
 
-    ms, flops, roof, kernels = bench_step(torch, qlora, synth, wl, args.steps, args.warmup)
-    value = flops / (ms * 1e-3) / 1e12
+    print(f"bench: {args.workload} set-up", file=sys.stderr, flush=True)
+    head = bench_workload(torch, qlora, synth, args.workload, args.steps, args.warmup)
+    value = head["value"]
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + " (NF4 + double quant base, LoRA fwd+bwd on every linear)",
-                   "tokens": wl.T, "r": wl.r, "alpha": wl.alpha,
-                   "linears": [[l.name, l.N, l.K] for l in wl.linears], "parallelism": "single GPU",
-                   "flop_per_step": flops},
-        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roof,
-        "kernels": kernels,
+        "config": {"workload": head["workload"] + " (NF4 + double quant base resident in HBM, LoRA fwd+bwd on "
+                               "every linear)",
+                   "tokens": head["tokens"], "r": head["r"], "alpha": head["alpha"], "layers": head["layers"],
+                   "linears": head["linears"], "parallelism": "single GPU", "flop_per_step": head["flop_per_step"]},
+        "frac_of_bf16_peak": head["frac_of_bf16_peak"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "quantize_all": head["quantize_all"],
     }
+    print(f"bench: {args.workload} {value} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_extras:
+        out["workloads"] = {}
+        for key in ("layer33b", "mlp7b"):
+            if key == args.workload:
+                continue
+            print(f"bench: {key}", file=sys.stderr, flush=True)
+            res = bench_workload(torch, qlora, synth, key, 10 if key == "layer33b" else 20, 3)
+            res.pop("kernels")
+            out["workloads"][key] = res
+        print("bench: gemv", file=sys.stderr, flush=True)
         out["gemv"] = bench_gemv(torch, qlora, synth)
+        print("bench: quantize", file=sys.stderr, flush=True)
         out["quantize"] = bench_quantize(torch, qlora)
+        print("bench: peaks", file=sys.stderr, flush=True)
+        peaks = measure_peaks(torch)
+        if peaks is not None:
+            peaks["headline_frac_of_measured_mfma"] = round(value / peaks["mfma_bf16_TFLOPs"], 4)
+            if head["roofline"]:
+                peaks["roofline_frac_of_measured_mfma"] = round(head["roofline"]["achieved"] /
+                                                               peaks["mfma_bf16_TFLOPs"], 4)
+            peaks["gemv_frac_of_measured_copy"] = round(out["gemv"]["value"] / peaks["copy_GBs"], 4)
+        out["peaks"] = peaks
     if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out))
 

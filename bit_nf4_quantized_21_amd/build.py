@@ -63,5 +63,19 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# The peak probes bench.py reads the measured MFMA and copy rates from (a
+# measurement aid beside the benchmark, not part of libqlora).
+PEAK_SRC = os.path.join(os.path.dirname(HERE), "bench_peaks.hip")
+PEAK_OUT = os.path.join(os.path.dirname(HERE), "bench_peaks.so")
+
+
+def build_peaks() -> str:
+    tmp = PEAK_OUT + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", PEAK_SRC, "-o", tmp])
+    os.replace(tmp, PEAK_OUT)
+    return PEAK_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_peaks())

@@ -1,4 +1,6 @@
-// Host-side construction of the NF4 codebook.
+// Host-side construction of the 4-bit decode tables: the NF4 codebook and
+// the two 4-bit types the pages compare NF4 with (news write-up, innovations
+// list: NF4 gives better results than 4-bit integers and 4-bit floats).
 //
 // NF4 is the 4-bit data type that is information-theoretically optimal for
 // normally distributed weights ("QLoRA: Efficient Finetuning of Quantized
@@ -15,6 +17,7 @@
 // fp64 ulp.
 #include <algorithm>
 #include <cmath>
+#include <utility>
 
 #include "codebook.hpp"
 
@@ -72,6 +75,53 @@ void build_codebook(float out[16]) {
   v[n++] = 0.0;
   std::sort(v, v + 16);
   for (int i = 0; i < 16; ++i) out[i] = (float)v[i];
+}
+
+// Int4: code = k mod 16 (4-bit two's complement), value k / 7 rounded to
+// fp32, k = -7..7 (symmetric absmax scaling; code 8, k = -8, is never
+// produced and decodes to -8/7).  FP4: OCP E2M1, code = sign << 3 |
+// exponent << 1 | mantissa with exponent bias 1 (subnormal when the exponent
+// field is 0), magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 divided by 6 so that
+// the largest is 1, rounded to fp32 (code 8, -0, is never produced).
+void build_type_table(int qtype, float out[16]) {
+  if (qtype == kQNF4) {
+    build_codebook(out);
+    return;
+  }
+  for (int c = 0; c < 16; ++c) {
+    if (qtype == kQINT4) {
+      const int k = c < 8 ? c : c - 16;
+      out[c] = (float)(k / 7.0);
+    } else {
+      const int e = (c >> 1) & 3, m = c & 1;
+      const double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * std::ldexp(1.0, e - 1);
+      const float v = (float)(mag / 6.0);
+      out[c] = (c & 8) ? -v : v;
+    }
+  }
+}
+
+void build_type_levels(int qtype, const float table[16], TypeLevels* out) {
+  int n = 0;
+  for (int c = 0; c < 16; ++c) {
+    if (qtype != kQNF4 && c == 8) continue;  // never produced
+    out->level[n] = table[c];
+    out->code[n] = (uint32_t)c;
+    ++n;
+  }
+  // insertion sort by value (16 entries)
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && out->level[j - 1] > out->level[j]; --j) {
+      std::swap(out->level[j - 1], out->level[j]);
+      std::swap(out->code[j - 1], out->code[j]);
+    }
+  out->n = n;
+  out->zero_code = 0;
+  for (int i = 0; i < n; ++i)
+    if (out->level[i] == 0.0f) {
+      out->zero_code = out->code[i];
+      break;
+    }
 }
 
 }  // namespace qlora

@@ -96,13 +96,23 @@ def dy_bits(T: int, N: int, i: int = 0) -> np.ndarray:
     return to_bf16_bits(_rng(5000 + i).normal(0.0, 1.0, size=(T, N)))
 
 
-def device_inputs(T, N, K, r, i=0, device="cuda", backward=True):
+def device_weight(out, i=0):
+    """Fill the fp32 device tensor `out` with the seeded N(0, 0.02) weight of
+    linear i (drawn on the device, for timing at full size)."""
+    import torch
+    g = torch.Generator(device=out.device)
+    g.manual_seed(1000 + i)
+    return out.normal_(0.0, 0.02, generator=g)
+
+
+def device_inputs(T, N, K, r, i=0, device="cuda", backward=True, weight=True):
     """Seeded inputs drawn directly on the device (for timing at full size)."""
     import torch
     g = torch.Generator(device=device)
     out = {}
-    g.manual_seed(1000 + i)
-    out["W"] = torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * 0.02
+    if weight:
+        g.manual_seed(1000 + i)
+        out["W"] = torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * 0.02
     g.manual_seed(2000 + i)
     out["X"] = torch.randn(T, K, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
     g.manual_seed(3000 + i)

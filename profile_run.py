@@ -1,9 +1,11 @@
 """Workload and summariser for rocprofv3 measurements of the NF4 linear kernels.
 
-`run` launches, on cuda:0, a few steps of the 7B MLP workload (gate/up
-4096->11008, down 11008->4096, 2048 tokens, LoRA r=64, fwd + bwd), a few
-small-token forwards (4096x4096, 4 tokens), and a plain copy of a known number
-of bytes that calibrates the HBM byte counters:
+`run` launches, on cuda:0, a few fwd+bwd steps of a workload's linears (by
+default two layers of the LLaMA-65B-shaped set: q/k/v/o 8192x8192, gate/up
+8192->22016, down 22016->8192, 512 tokens, LoRA r=64; every layer has the
+same shapes, so per-launch figures are those of the 80-layer set), a few
+small-token forwards (4096x4096, 4 tokens), and a plain copy of a known
+number of bytes that calibrates the HBM byte counters:
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o fetch -- \
         python profile_run.py run
@@ -23,7 +25,7 @@ statistics file into a short markdown table.
     rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d OUT/mfma -o mfma -- \
         python profile_run.py run
 
-into profiles/mfma_mlp7b_gemv7b.md: per kernel the share of SIMD cycles with
+into profiles/mfma_<workload>.md: per kernel the share of SIMD cycles with
 the matrix cores busy (MfmaUtil, percent) and the bf16 MFMA flops executed
 per launch beside the algorithmic flops.
 """
@@ -32,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -45,17 +48,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 COPY_BYTES = 512 << 20
-MLP = (("gate_proj", 11008, 4096), ("up_proj", 11008, 4096), ("down_proj", 4096, 11008))
-T_MLP, R, ALPHA = 2048, 64, 16.0
+R, ALPHA = 64, 16.0
 GEMV = (4, 4096, 4096)
 
-# kernel -> (workload tag, sources it is built from)
+# kernel -> sources it is built from
 KERNEL_SOURCES = {
-    "gemm_fwd_kernel": ("mlp7b", ["gemm_fwd.hip", "gemm.hpp", "splitk.hpp", "common.hpp"]),
-    "gemm_dx_kernel": ("mlp7b", ["gemm_dx.hip", "gemm.hpp", "splitk.hpp", "common.hpp"]),
-    "tokdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
-    "rowdot_partial_kernel": ("mlp7b", ["lora.hip", "lora.hpp", "common.hpp"]),
-    "gemv_fwd_kernel": ("gemv7b", ["gemv.hip", "gemm.hpp", "common.hpp"]),
+    "gemm_fwd_kernel": ["gemm_fwd.hip", "gemm.hpp", "splitk.hpp", "common.hpp"],
+    "gemm_dx_kernel": ["gemm_dx.hip", "gemm.hpp", "splitk.hpp", "common.hpp"],
+    "tokdot_partial_kernel": ["lora.hip", "lora.hpp", "common.hpp"],
+    "rowdot_partial_kernel": ["lora.hip", "lora.hpp", "common.hpp"],
+    "gemv_fwd_kernel": ["gemv.hip", "gemm.hpp", "common.hpp"],
 }
 
 
@@ -93,30 +95,30 @@ def algorithmic_flops(kernel, T, N, K, r):
     return None
 
 
-def run(steps):
+def workload_shapes(workload):
+    from bit_nf4_quantized_21_amd import synth
+    wl = synth.WORKLOADS[workload]
+    return wl.T, [(l.N, l.K) for l in wl.linears]
+
+
+def run(workload, layers, steps):
     import torch
+    import bench
     from bit_nf4_quantized_21_amd import qlora, synth
     qlora.lib()
-    dev = torch.device("cuda", 0)
-    layers = []
-    for i, (_, N, K) in enumerate(MLP):
-        inp = synth.device_inputs(T_MLP, N, K, R, i, backward=True)
-        qlora.quantize_nf4(inp["W"].view(-1).to(torch.bfloat16))  # the same weights stored as bf16
-        codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
-        q8, s2 = qlora.double_quant(absmax)
-        del inp["W"], absmax
-        L = dict(N=N, codes=codes, q8=q8, s2=s2, **inp)
-        L["wsf"] = torch.empty(max(1, qlora.linear_fwd_workspace_bytes(T_MLP, K, N, R)), dtype=torch.uint8, device=dev)
-        L["wsb"] = torch.empty(max(1, qlora.linear_bwd_workspace_bytes(T_MLP, K, N, R)), dtype=torch.uint8, device=dev)
-        layers.append(L)
+    wl = synth.WORKLOADS[workload]
+    wl = dataclasses.replace(wl, layers=min(layers, wl.layers))
+    lins = bench.linear_list(wl)
+    weights, _ = bench.quantize_all(torch, qlora, synth, wl, lins)
+    Ls = bench.make_linears(torch, qlora, synth, wl, lins, weights)
+    del weights
     for _ in range(steps):
-        for L in layers:
-            Y, XA = qlora.linear_fwd(L["X"], L["codes"], L["q8"], L["s2"], L["A"], L["B"], ALPHA, L["N"],
-                                     workspace=L["wsf"])
-            qlora.linear_bwd(L["dY"], L["X"], XA, L["codes"], L["q8"], L["s2"], L["A"], L["B"], ALPHA,
-                             workspace=L["wsb"])
+        for L in Ls:
+            bench.run_fwd(qlora, L, wl.alpha)
+        for L in reversed(Ls):
+            bench.run_bwd(qlora, L, wl.alpha)
     torch.cuda.synchronize()
-    del layers
+    del Ls
     T, N, K = GEMV
     inp = synth.device_inputs(T, N, K, R, 0, backward=False)
     codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))
@@ -124,7 +126,7 @@ def run(steps):
     for _ in range(steps):
         qlora.linear_fwd(inp["X"], codes, q8, s2, inp["A"], inp["B"], ALPHA, N)
     torch.cuda.synchronize()
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(steps):
         dst.copy_(src)
@@ -161,7 +163,7 @@ def copy_factor(rows):
     return (sum(vals) / len(vals)) / (COPY_BYTES / 1024)
 
 
-def traffic(fetch_dir, write_dir, command):
+def traffic(fetch_dir, write_dir, command, workload):
     fr, wr = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
     ff, wf = copy_factor(fr), copy_factor(wr)
     os.makedirs(PROFILES, exist_ok=True)
@@ -171,15 +173,17 @@ def traffic(fetch_dir, write_dir, command):
              f"{ff:.4f}x, WRITE_SIZE {wf:.4f}x the true bytes; the figures below are divided by these.", "",
              "| kernel | workload | launches | fetch MB | write MB | total MB/launch | algorithmic MB/launch | ratio |",
              "|---|---|---|---|---|---|---|---|"]
-    for kernel, (wl, sources) in KERNEL_SOURCES.items():
+    T_w, shapes = workload_shapes(workload)
+    for kernel, sources in KERNEL_SOURCES.items():
+        wl = "gemv7b" if kernel == "gemv_fwd_kernel" else workload
         f = [v for (k, g, v) in fr if short_name(k) == kernel]
         w = [v for (k, g, v) in wr if short_name(k) == kernel]
         if not f or not w:
             continue
         fb = sum(f) / len(f) * 1024 / ff
         wb = sum(w) / len(w) * 1024 / wf
-        if wl == "mlp7b":
-            alg = [algorithmic_bytes(kernel, T_MLP, N, K, R) for (_, N, K) in MLP]
+        if wl == workload:
+            alg = [algorithmic_bytes(kernel, T_w, N, K, R) for (N, K) in shapes]
         else:
             alg = [algorithmic_bytes(kernel, *GEMV, R)]
         alg_b = None if alg[0] is None else sum(alg) / len(alg)
@@ -194,7 +198,7 @@ def traffic(fetch_dir, write_dir, command):
         algs = "" if alg_b is None else f"{alg_b / 1e6:.1f}"
         lines.append(f"| {kernel} | {wl} | {len(f)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | "
                      f"{algs} | {ratio} |")
-    with open(os.path.join(PROFILES, "traffic_mlp7b_gemv7b.md"), "w") as fo:
+    with open(os.path.join(PROFILES, f"traffic_{workload}_gemv7b.md"), "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -215,7 +219,7 @@ def stats(stats_csv, out_md, command, top=12):
     print("\n".join(lines))
 
 
-def mfma(pmc_dir, command):
+def mfma(pmc_dir, command, workload):
     util, flops = read_counter(pmc_dir, "MfmaUtil"), read_counter(pmc_dir, "MfmaFlopsBF16")
     kernels = list(KERNEL_SOURCES) + ["xa_partial_kernel", "rowdot_reduce_kernel", "tokdot_reduce_kernel"]
     lines = ["# MFMA utilisation per kernel (rocprofv3 MfmaUtil, MfmaFlopsBF16)", "",
@@ -230,16 +234,17 @@ def mfma(pmc_dir, command):
         f = [v for (k, g, v) in flops if short_name(k) == kernel]
         if not u:
             continue
-        wl = KERNEL_SOURCES.get(kernel, ("mlp7b" if "gemv" not in kernel and "xa_" not in kernel else "gemv7b",))[0]
-        if wl == "mlp7b":
-            alg = [algorithmic_flops(kernel, T_MLP, N, K, R) for (_, N, K) in MLP]
+        wl = "gemv7b" if ("gemv" in kernel or "xa_" in kernel) else workload
+        T_w, shapes = workload_shapes(workload)
+        if wl == workload:
+            alg = [algorithmic_flops(kernel, T_w, N, K, R) for (N, K) in shapes]
         else:
             alg = [algorithmic_flops(kernel, *GEMV, R)]
         algs = "" if alg[0] is None else f"{sum(alg) / len(alg) / 1e9:.1f}"
         fs = f"{sum(f) / len(f) / 1e9:.1f}" if f else ""
         lines.append(f"| {kernel} | {wl} | {len(u)} | {sum(u) / len(u):.1f} | {fs} | {algs} |")
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, "mfma_mlp7b_gemv7b.md"), "w") as fo:
+    with open(os.path.join(PROFILES, f"mfma_{workload}_gemv7b.md"), "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -249,24 +254,28 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--steps", type=int, default=2)
+    r.add_argument("--workload", default="full65b")
+    r.add_argument("--layers", type=int, default=2)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("--command", required=True)
+    t.add_argument("--workload", default="full65b")
     m = sub.add_parser("mfma")
     m.add_argument("pmc_dir")
     m.add_argument("--command", required=True)
+    m.add_argument("--workload", default="full65b")
     s = sub.add_parser("stats")
     s.add_argument("stats_csv")
     s.add_argument("out_md")
     s.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "run":
-        run(a.steps)
+        run(a.workload, a.layers, a.steps)
     elif a.cmd == "traffic":
-        traffic(a.fetch_dir, a.write_dir, a.command)
+        traffic(a.fetch_dir, a.write_dir, a.command, a.workload)
     elif a.cmd == "mfma":
-        mfma(a.pmc_dir, a.command)
+        mfma(a.pmc_dir, a.command, a.workload)
     else:
         stats(a.stats_csv, a.out_md, a.command)
 
