@@ -14,9 +14,15 @@ namespace qlora {
 namespace {
 __device__ __align__(256) int g_status_word;
 
+// Workspace of qlora_linear_fwd_noalloc, for callers that cannot allocate
+// device memory (graph capture, tight serving loops).  Every GPU holds its
+// own copy until the process ends; every call on a GPU shares it.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 int* g_status_ptr[kMaxDevices] = {};
+void* g_scratch_ptr[kMaxDevices] = {};
 }  // namespace
 
 int* status_word(hipError_t* err) {
@@ -39,6 +45,28 @@ int* status_word(hipError_t* err) {
   }
   *err = hipSuccess;
   return g_status_ptr[dev];
+}
+
+void* noalloc_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with this device current
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
 }
 
 hipError_t take_status(hipStream_t s, int* bits) {

@@ -68,6 +68,8 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported blocksize or rank";
     case QLORA_ERR_HIP: return "QLORA_ERR_HIP: a HIP call failed (see qlora_last_hip_error)";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_SCRATCH:
+      return "QLORA_ERR_SCRATCH: the problem needs more scratch than the no-allocation entry point holds";
     case QLORA_ERR_DEVICE:
       return "QLORA_ERR_DEVICE: a kernel's bounded wait ran out; results since the last status query are unreliable";
     default: return "unknown qlora_status";
@@ -162,6 +164,24 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N, const u
   if (need && !aligned16(workspace)) return QLORA_ERR_ALIGN;
   qlora::LinearArgs a{T, K, N, r, (float)(alpha / (float)r), codes, q8, s2, A, B};
   return hip_status(qlora::launch_linear_fwd(a, tables().cb, X, Y, XA, workspace, (hipStream_t)stream));
+}
+
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                             const uint8_t* q8, const float* s2, const uint16_t* A, const uint16_t* B, int32_t r,
+                             float alpha, uint16_t* Y, float* XA, void* stream) {
+  int st = check_linear_shape(T, K, N, r);
+  if (st != QLORA_OK) return st;
+  if (T == 0) return QLORA_OK;
+  if (!X || !codes || !q8 || !s2 || !A || !B || !Y || !XA) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(codes) || !aligned16(q8) || !aligned16(s2) || !aligned16(A) || !aligned16(B) ||
+      !aligned16(Y) || !aligned16(XA))
+    return QLORA_ERR_ALIGN;
+  if (qlora::fwd_workspace_bytes(T, K, N, r) > qlora::kNoallocScratchBytes) return QLORA_ERR_SCRATCH;
+  hipError_t e = hipSuccess;
+  void* ws = qlora::noalloc_scratch(&e);
+  if (!ws) return hip_status(e);
+  qlora::LinearArgs a{T, K, N, r, (float)(alpha / (float)r), codes, q8, s2, A, B};
+  return hip_status(qlora::launch_linear_fwd(a, tables().cb, X, Y, XA, ws, (hipStream_t)stream));
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA, int64_t T, int64_t K, int64_t N,

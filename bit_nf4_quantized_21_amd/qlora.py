@@ -28,6 +28,8 @@ _SIGNATURES = {
     "qlora_linear_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
     "qlora_linear_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_f,
                                         _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                                _c_f, _c_p, _c_p, _c_p]),
     "qlora_linear_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                         _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "qlora_timing_enable": (None, [ctypes.c_int]),
@@ -241,6 +243,28 @@ def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None
     workspace = _workspace(nbytes, X.device, workspace)
     _check(lib().qlora_linear_fwd(_p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r, float(alpha),
                                   _p(Y), _p(XA), _p(workspace), nbytes, _stream(stream)))
+    return Y, XA
+
+
+def linear_fwd_noalloc(X, codes, q8, s2, A, B, alpha, N, Y, XA, stream=None):
+    """linear_fwd with the library's static scratch as workspace: allocates
+    nothing (Y and XA are the caller's).  Calls on one GPU must not overlap."""
+    torch = _torch()
+    _dev(X, torch.bfloat16, "X")
+    _dev(A, torch.bfloat16, "A")
+    _dev(B, torch.bfloat16, "B")
+    _dev(codes, torch.uint8, "codes")
+    _dev(q8, torch.uint8, "q8")
+    _dev(s2, torch.float32, "s2")
+    T, K = X.shape
+    r = A.shape[1]
+    if A.shape != (K, r) or B.shape != (r, N):
+        raise ValueError("A must be [K,r] and B [r,N]")
+    _weight(codes, q8, s2, N, K)
+    _need(_dev(Y, torch.bfloat16, "Y"), T * N, "Y")
+    _need(_dev(XA, torch.float32, "XA"), T * r, "XA")
+    _check(lib().qlora_linear_fwd_noalloc(_p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r, float(alpha),
+                                          _p(Y), _p(XA), _stream(stream)))
     return Y, XA
 
 

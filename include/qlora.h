@@ -53,7 +53,8 @@ typedef enum {
   QLORA_ERR_UNSUPPORTED = -4, /* blocksize != 64 / 256, rank outside [8,128] or not a multiple of 8 */
   QLORA_ERR_HIP = -5,         /* a HIP launch or query failed; see qlora_last_hip_error() */
   QLORA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
-  QLORA_ERR_DEVICE = -7       /* a kernel's bounded wait ran out (reported by qlora_device_status) */
+  QLORA_ERR_DEVICE = -7,      /* a kernel's bounded wait ran out (reported by qlora_device_status) */
+  QLORA_ERR_SCRATCH = -8      /* the problem needs more than the no-allocation entry point's scratch */
 } qlora_status;
 
 /*
@@ -149,6 +150,27 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N,
                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                      uint16_t* Y, float* XA,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward without any device allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same computation, kernels, arguments and results as
+ * qlora_linear_fwd, but the workspace is the library's own static device
+ * array of 80 MiB (QLORA_NOALLOC_SCRATCH_BYTES) on each GPU, held until the
+ * process ends; the call itself allocates nothing.  A problem whose
+ * qlora_linear_fwd_workspace_bytes exceeds it returns QLORA_ERR_SCRATCH
+ * before anything is enqueued (every configuration of this library's
+ * benchmarks needs at most 69 MiB).  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller.  The kernels clear the
+ * counters they need at the start of each call, so leftover contents from an
+ * earlier call never matter.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES (80u << 20)
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N,
+                             const uint8_t* codes, const uint8_t* q8, const float* s2,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             uint16_t* Y, float* XA, void* stream);
 
 /*
  * Backward of the same layer (Abstract: backpropagation through the frozen
