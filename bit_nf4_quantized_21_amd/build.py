@@ -36,7 +36,7 @@ def _run(cmd):
 
 def sources():
     hip = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    return hip, ["qlora_api.cpp", "timing.cpp"], ["codebook.cpp"]
+    return hip, ["qlora_api.cpp", "timing.cpp", "storage.cpp"], ["codebook.cpp"]
 
 
 def build(verbose: bool = False) -> str:

@@ -20,9 +20,17 @@ constexpr int kBlock2 = 256;  // absmax constants per second-level group
 struct Codebook {
   float c[16];
 };
+// Decision data of a stored 4-bit type: the boundaries between its sorted
+// distinct levels (exact in fp64; +inf past the type's last), the code of
+// sorted level i in bits 4i..4i+3 of `codes`, and the code of the value 0.
 struct Midpoints {
   double m[15];
+  uint64_t codes;
+  uint32_t zero_code;
 };
+__host__ __device__ __forceinline__ uint32_t level_code(const Midpoints& mp, uint32_t level) {
+  return (uint32_t)(mp.codes >> (4 * level)) & 15u;
+}
 
 // Writes the codebook to lut[0..15] (16-byte aligned) from thread 0 with
 // four vector stores of the kernel argument's values.  No lane-indexed read

@@ -2,6 +2,7 @@
 // validation, the codebook, and dispatch to the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -12,26 +13,72 @@
 #include "common.hpp"
 #include "device_state.hpp"
 #include "kernels.hpp"
+#include "storage.hpp"
 #include "timing.hpp"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
 
-struct Tables {
+// Decode table and decision data of each stored 4-bit type, built once.
+struct TypeTables {
   qlora::Codebook cb;
   qlora::Midpoints mp;
+  bool exact;  // every level boundary times a 24-bit absmax is exact in fp64
+};
+
+// Significant bits of a finite double (0 for 0).
+int significant_bits(double x) {
+  if (x == 0.0) return 0;
+  int e = 0;
+  double f = std::frexp(std::fabs(x), &e);  // f in [0.5, 1)
+  int bits = 0;
+  while (f != 0.0 && bits < 64) {
+    f = f * 2.0;
+    const double d = std::floor(f);
+    f -= d;
+    ++bits;
+  }
+  return bits;
+}
+
+struct Tables {
+  TypeTables t[qlora::kQTypes];
 };
 
 const Tables& tables() {
   static Tables t;
   static std::once_flag once;
   std::call_once(once, [] {
-    qlora::build_codebook(t.cb.c);
-    // Decision boundaries between neighbouring codes, exact in fp64.
-    for (int j = 0; j < 15; ++j) t.mp.m[j] = ((double)t.cb.c[j] + (double)t.cb.c[j + 1]) / 2.0;
+    for (int q = 0; q < qlora::kQTypes; ++q) {
+      TypeTables& tt = t.t[q];
+      qlora::build_type_table(q, tt.cb.c);
+      qlora::TypeLevels lv{};
+      qlora::build_type_levels(q, tt.cb.c, &lv);
+      tt.exact = true;
+      tt.mp.codes = 0;
+      for (int i = 0; i < lv.n; ++i) tt.mp.codes |= (uint64_t)lv.code[i] << (4 * i);
+      for (int i = lv.n; i < 16; ++i) tt.mp.codes |= (uint64_t)lv.code[lv.n - 1] << (4 * i);
+      tt.mp.zero_code = lv.zero_code;
+      // Boundaries between neighbouring levels, exact in fp64 (two fp32
+      // values a few binades apart add exactly; halving is exact).
+      for (int j = 0; j < 15; ++j) {
+        if (j + 1 < lv.n) {
+          tt.mp.m[j] = ((double)lv.level[j] + (double)lv.level[j + 1]) / 2.0;
+          if (significant_bits(tt.mp.m[j]) > 29) tt.exact = false;
+        } else {
+          tt.mp.m[j] = HUGE_VAL;
+        }
+      }
+    }
   });
   return t;
+}
+
+const TypeTables* type_tables(int32_t qtype) {
+  if (qtype < 0 || qtype >= qlora::kQTypes) return nullptr;
+  const TypeTables& tt = tables().t[qtype];
+  return tt.exact ? &tt : nullptr;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -56,7 +103,15 @@ int check_linear_shape(int64_t T, int64_t K, int64_t N, int32_t r) {
 extern "C" {
 
 void qlora_nf4_codebook(float out[16]) {
-  if (out) std::memcpy(out, tables().cb.c, sizeof(float) * 16);
+  if (out) std::memcpy(out, tables().t[qlora::kQNF4].cb.c, sizeof(float) * 16);
+}
+
+int qlora_4bit_table(int32_t qtype, float out[16]) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
+  if (!out) return QLORA_ERR_NULL;
+  std::memcpy(out, tt->cb.c, sizeof(float) * 16);
+  return QLORA_OK;
 }
 
 const char* qlora_status_string(int status) {
@@ -68,6 +123,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED: unsupported blocksize or rank";
     case QLORA_ERR_HIP: return "QLORA_ERR_HIP: a HIP call failed (see qlora_last_hip_error)";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_IO: return "QLORA_ERR_IO: file missing, unreadable, malformed or of another shape or type";
     case QLORA_ERR_SCRATCH:
       return "QLORA_ERR_SCRATCH: the problem needs more scratch than the no-allocation entry point holds";
     case QLORA_ERR_DEVICE:
@@ -99,24 +155,42 @@ int qlora_timing_read(char* buf, size_t buflen) {
   return (int)text.size();
 }
 
-int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize, uint8_t* codes, float* absmax,
-                       void* stream) {
-  if (blocksize != 64) return QLORA_ERR_UNSUPPORTED;
+int qlora_quantize_4bit(const void* W, int32_t w_is_bf16, int64_t n, int32_t blocksize, int32_t qtype,
+                        uint8_t* codes, float* absmax, void* stream) {
+  if (blocksize != 64 || (w_is_bf16 != 0 && w_is_bf16 != 1)) return QLORA_ERR_UNSUPPORTED;
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
   if (n < 0 || n % 2 != 0 || n > (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (n == 0) return QLORA_OK;
   if (!W || !codes || !absmax) return QLORA_ERR_NULL;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
-  return hip_status(qlora::launch_quantize_nf4(W, n, codes, absmax, tables().mp, (hipStream_t)stream));
+  if (w_is_bf16)
+    return hip_status(qlora::launch_quantize_nf4_bf16(static_cast<const uint16_t*>(W), n, codes, absmax, tt->mp,
+                                                      (hipStream_t)stream));
+  return hip_status(
+      qlora::launch_quantize_nf4(static_cast<const float*>(W), n, codes, absmax, tt->mp, (hipStream_t)stream));
+}
+
+int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize, uint8_t* codes, float* absmax,
+                       void* stream) {
+  return qlora_quantize_4bit(W, 0, n, blocksize, qlora::kQNF4, codes, absmax, stream);
 }
 
 int qlora_quantize_nf4_bf16(const uint16_t* W, int64_t n, int32_t blocksize, uint8_t* codes, float* absmax,
                             void* stream) {
-  if (blocksize != 64) return QLORA_ERR_UNSUPPORTED;
+  return qlora_quantize_4bit(W, 1, n, blocksize, qlora::kQNF4, codes, absmax, stream);
+}
+
+int qlora_quantize_dq(const void* W, int32_t w_is_bf16, int64_t n, int32_t qtype, uint8_t* codes, uint8_t* q8,
+                      float* s2, void* stream) {
+  if (w_is_bf16 != 0 && w_is_bf16 != 1) return QLORA_ERR_UNSUPPORTED;
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
   if (n < 0 || n % 2 != 0 || n > (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (n == 0) return QLORA_OK;
-  if (!W || !codes || !absmax) return QLORA_ERR_NULL;
-  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
-  return hip_status(qlora::launch_quantize_nf4_bf16(W, n, codes, absmax, tables().mp, (hipStream_t)stream));
+  if (!W || !codes || !q8 || !s2) return QLORA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(q8) || !aligned16(s2)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_quantize_dq(W, w_is_bf16 != 0, n, codes, q8, s2, tt->mp, (hipStream_t)stream));
 }
 
 int qlora_double_quant(const float* absmax, int64_t nb, int32_t blocksize2, uint8_t* q8, float* s2,
@@ -129,14 +203,21 @@ int qlora_double_quant(const float* absmax, int64_t nb, int32_t blocksize2, uint
   return hip_status(qlora::launch_double_quant(absmax, nb, q8, s2, (hipStream_t)stream));
 }
 
-int qlora_dequantize_nf4(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
-                         int32_t out_is_bf16, void* out, void* stream) {
+int qlora_dequantize_4bit(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n, int32_t qtype,
+                          int32_t out_is_bf16, void* out, void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
   if (n < 0 || n % 2 != 0 || n > (int64_t(1) << 40)) return QLORA_ERR_SHAPE;
   if (out_is_bf16 != 0 && out_is_bf16 != 1) return QLORA_ERR_UNSUPPORTED;
   if (n == 0) return QLORA_OK;
   if (!codes || !q8 || !s2 || !out) return QLORA_ERR_NULL;
   if (!aligned16(codes) || !aligned16(q8) || !aligned16(s2) || !aligned16(out)) return QLORA_ERR_ALIGN;
-  return hip_status(qlora::launch_dequantize(codes, q8, s2, n, out_is_bf16, out, tables().cb, (hipStream_t)stream));
+  return hip_status(qlora::launch_dequantize(codes, q8, s2, n, out_is_bf16, out, tt->cb, (hipStream_t)stream));
+}
+
+int qlora_dequantize_nf4(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n,
+                         int32_t out_is_bf16, void* out, void* stream) {
+  return qlora_dequantize_4bit(codes, q8, s2, n, qlora::kQNF4, out_is_bf16, out, stream);
 }
 
 size_t qlora_linear_fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r) {
@@ -149,9 +230,12 @@ size_t qlora_linear_bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t
   return qlora::bwd_workspace_bytes(T, K, N, r);
 }
 
-int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* q8,
-                     const float* s2, const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
-                     float* XA, void* workspace, size_t workspace_bytes, void* stream) {
+int qlora_linear_fwd_4bit(int32_t qtype, const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                          const uint8_t* q8, const float* s2, const uint16_t* A, const uint16_t* B, int32_t r,
+                          float alpha, uint16_t* Y, float* XA, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
   int st = check_linear_shape(T, K, N, r);
   if (st != QLORA_OK) return st;
   if (T == 0) return QLORA_OK;
@@ -163,7 +247,14 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N, const u
   if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return QLORA_ERR_ALIGN;
   qlora::LinearArgs a{T, K, N, r, (float)(alpha / (float)r), codes, q8, s2, A, B};
-  return hip_status(qlora::launch_linear_fwd(a, tables().cb, X, Y, XA, workspace, (hipStream_t)stream));
+  return hip_status(qlora::launch_linear_fwd(a, tt->cb, X, Y, XA, workspace, (hipStream_t)stream));
+}
+
+int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes, const uint8_t* q8,
+                     const float* s2, const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                     float* XA, void* workspace, size_t workspace_bytes, void* stream) {
+  return qlora_linear_fwd_4bit(qlora::kQNF4, X, T, K, N, codes, q8, s2, A, B, r, alpha, Y, XA, workspace,
+                               workspace_bytes, stream);
 }
 
 int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
@@ -181,13 +272,15 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N,
   void* ws = qlora::noalloc_scratch(&e);
   if (!ws) return hip_status(e);
   qlora::LinearArgs a{T, K, N, r, (float)(alpha / (float)r), codes, q8, s2, A, B};
-  return hip_status(qlora::launch_linear_fwd(a, tables().cb, X, Y, XA, ws, (hipStream_t)stream));
+  return hip_status(qlora::launch_linear_fwd(a, tables().t[qlora::kQNF4].cb, X, Y, XA, ws, (hipStream_t)stream));
 }
 
-int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA, int64_t T, int64_t K, int64_t N,
-                     const uint8_t* codes, const uint8_t* q8, const float* s2, const uint16_t* A, const uint16_t* B,
-                     int32_t r, float alpha, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int qlora_linear_bwd_4bit(int32_t qtype, const uint16_t* dY, const uint16_t* X, const float* XA, int64_t T,
+                          int64_t K, int64_t N, const uint8_t* codes, const uint8_t* q8, const float* s2,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* dX, uint16_t* dA,
+                          uint16_t* dB, void* workspace, size_t workspace_bytes, void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
   int st = check_linear_shape(T, K, N, r);
   if (st != QLORA_OK) return st;
   if (!dA || !dB) return QLORA_ERR_NULL;
@@ -200,8 +293,52 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA, int
   if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return QLORA_ERR_ALIGN;
   qlora::LinearArgs a{T, K, N, r, (float)(alpha / (float)r), codes, q8, s2, A, B};
-  return hip_status(
-      qlora::launch_linear_bwd(a, tables().cb, dY, X, XA, dX, dA, dB, workspace, (hipStream_t)stream));
+  return hip_status(qlora::launch_linear_bwd(a, tt->cb, dY, X, XA, dX, dA, dB, workspace, (hipStream_t)stream));
+}
+
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA, int64_t T, int64_t K, int64_t N,
+                     const uint8_t* codes, const uint8_t* q8, const float* s2, const uint16_t* A, const uint16_t* B,
+                     int32_t r, float alpha, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return qlora_linear_bwd_4bit(qlora::kQNF4, dY, X, XA, T, K, N, codes, q8, s2, A, B, r, alpha, dX, dA, dB, workspace,
+                               workspace_bytes, stream);
+}
+
+int qlora_save_4bit(const char* path, int32_t qtype, int64_t N, int64_t K, const uint8_t* codes, const uint8_t* q8,
+                    const float* s2, void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
+  if (N <= 0 || K <= 0 || (N * K) % 2 != 0 || N > (int64_t(1) << 28) || K > (int64_t(1) << 28)) return QLORA_ERR_SHAPE;
+  if (!path || !codes || !q8 || !s2) return QLORA_ERR_NULL;
+  hipError_t e = hipSuccess;
+  const int rc = qlora::save_4bit(path, qtype, tt->cb.c, N, K, codes, q8, s2, (hipStream_t)stream, &e);
+  if (rc == qlora::kStorageHip) return hip_status(e);
+  return rc == qlora::kStorageOk ? QLORA_OK : QLORA_ERR_IO;
+}
+
+int qlora_load_4bit_info(const char* path, int32_t* qtype, int64_t* N, int64_t* K) {
+  if (!path || !qtype || !N || !K) return QLORA_ERR_NULL;
+  const float* tabs[3] = {tables().t[0].cb.c, tables().t[1].cb.c, tables().t[2].cb.c};
+  int q = 0;
+  hipError_t e = hipSuccess;
+  const int rc = qlora::load_4bit(path, tabs, &q, N, K, nullptr, nullptr, nullptr, 0, 0, 0, &e);
+  if (rc != qlora::kStorageOk) return QLORA_ERR_IO;
+  *qtype = q;
+  return QLORA_OK;
+}
+
+int qlora_load_4bit(const char* path, int32_t qtype, int64_t N, int64_t K, uint8_t* codes, uint8_t* q8, float* s2,
+                    void* stream) {
+  if (!type_tables(qtype)) return QLORA_ERR_UNSUPPORTED;
+  if (!path || !codes || !q8 || !s2) return QLORA_ERR_NULL;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  const float* tabs[3] = {tables().t[0].cb.c, tables().t[1].cb.c, tables().t[2].cb.c};
+  int q = 0;
+  int64_t n_ = 0, k_ = 0;
+  const int rc = qlora::load_4bit(path, tabs, &q, &n_, &k_, codes, q8, s2, qtype, N, K, &e);
+  if (rc == qlora::kStorageHip) return hip_status(e);
+  return rc == qlora::kStorageOk ? QLORA_OK : QLORA_ERR_IO;
 }
 
 }  // extern "C"

@@ -1,17 +1,21 @@
-// Blockwise NF4 quantization, double quantization and dequantization kernels
-// for gfx950.
+// Blockwise 4-bit quantization, double quantization and dequantization
+// kernels for gfx950.
 //
 // NF4 and double quantization are items (a) and (b) of the QLoRA abstract
-// ("QLoRA: Efficient Finetuning of Quantized LLMs"); the block sizes (64 and
-// 256), the 8-bit constant format and the low-nibble-first packing are the
-// readings documented in include/qlora.h.
+// ("QLoRA: Efficient Finetuning of Quantized LLMs"); Int4 and FP4 are the
+// 4-bit types the pages compare NF4 with (news write-up, innovations list).
+// The block sizes (64 and 256), the 8-bit constant format, the decode tables
+// and the low-nibble-first packing are the readings documented in
+// include/qlora.h.  Every type is quantized by the same rule: the code of the
+// type's level nearest to w/absmax in exact arithmetic.
 //
-// All three kernels are HBM-bound streams.  The quantizer gives each 64-weight
-// block to 16 lanes (one 16-byte load per lane, a 4-step shuffle max for the
-// absmax), four blocks per lane group with their loads issued together, and
-// decides every code exactly with fp64 products against the fp64 midpoints
-// of the codebook; the double quantizer gives each group of 256
-// constants to one wavefront.
+// All kernels are HBM-bound streams.  A 64-weight block belongs to 16 lanes
+// (one 16-byte load per lane, a 4-step shuffle max for the absmax); each
+// 16-lane group takes four blocks with their loads issued together.  Codes
+// are decided exactly with fp64 products against the fp64 level boundaries.
+// The double quantizer gives each group of 256 constants to one wavefront;
+// the fused quantizer gives each group of 256 blocks to one workgroup and
+// keeps the absmax values on chip.
 #include <cmath>
 
 #include "common.hpp"
@@ -21,16 +25,8 @@
 namespace qlora {
 
 // ---------------------------------------------------------------------------
-// Quantize: W[n] fp32 -> codes[n/2], absmax[ceil(n/64)].
+// Quantize: W[n] fp32 or bf16 -> codes[n/2], absmax[ceil(n/64)].
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t nf4_code(float w, double a64, const double* thr) {
-  // code = #{j : w > absmax * m_j}; thr[j] = absmax * m_j is exact in fp64.
-  double w64 = (double)w;
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < 15; ++j) c += (w64 > thr[j]) ? 1u : 0u;
-  return a64 == 0.0 ? 7u : c;
-}
 
 // Each 16-lane group quantizes kQGroupBlocks consecutive blocks; the loads of
 // all of them are issued before any is used, so a wave keeps 4 KiB (fp32) or
@@ -62,20 +58,32 @@ __device__ __forceinline__ void load_weights4(const uint16_t* __restrict__ W, in
     for (int i = 0; i < 4; ++i) v[i] = (e0 + i < n) ? __uint_as_float((uint32_t)W[e0 + i] << 16) : 0.0f;
   }
 }
+
 constexpr int kBins = 128;             // uniform bins of w / absmax over [-1, 1]
 constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
 
-// Nearest code by bins: every bin of width 2/kBins holds at most one decision
-// boundary m_j, none within 1e-5 of a bin edge (checked on the host), so the
-// bin of the fp32 estimate x = w * (1/absmax) (error < 1e-6) contains x's
-// true position or is a neighbour separated from it by no boundary.  The code
-// is the number of boundaries below the bin plus the exact fp64 decision
-// w > absmax * m_j for the bin's own boundary (m = +inf when it has none).
-template <typename T>
-__device__ __forceinline__ void quantize_nf4_binned(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
-                                                    float* __restrict__ absmax, const Midpoints& mp) {
-  __shared__ double s_thr[kBins];
-  __shared__ uint32_t s_lo[kBins];
+// Exact scan: level = #{j : w > absmax * m_j} over the type's boundaries
+// (absmax * m_j is exact in fp64; +inf boundaries never count).
+__device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoints& mp) {
+  const double w64 = (double)w;
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (w64 > a64 * mp.m[j]) ? 1u : 0u;
+  return a64 == 0.0 ? mp.zero_code : level_code(mp, c);
+}
+
+// Bin tables of a type in LDS: every bin of width 2/kBins holds at most one
+// level boundary, none within 1e-5 of a bin edge (checked on the host before
+// the binned kernels are chosen), so the bin of the fp32 estimate
+// x = w * (1/absmax) (error < 1e-6) contains x's true position or is a
+// neighbour separated from it by no boundary.  thr[b] is the bin's boundary
+// (+inf when it has none); code[b] holds the code below it in bits 0..7 and
+// the code above it in bits 8..15.
+struct BinTables {
+  double thr[kBins];
+  uint32_t code[kBins];
+};
+__device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const Midpoints& mp) {
   if (threadIdx.x < kBins) {
     const double lo = -1.0 + threadIdx.x * (2.0 / kBins), hi = lo + 2.0 / kBins;
     uint32_t cnt = 0;
@@ -85,10 +93,57 @@ __device__ __forceinline__ void quantize_nf4_binned(const T* __restrict__ W, int
       if (mp.m[j] < lo) cnt += 1;
       else if (mp.m[j] < hi) thr = mp.m[j];
     }
-    s_thr[threadIdx.x] = thr;
-    s_lo[threadIdx.x] = cnt;
+    t.thr[threadIdx.x] = thr;
+    t.code[threadIdx.x] = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 8);
   }
-  __syncthreads();
+}
+
+// Quantizes the block held by a 16-lane group (lane l16 holds elements
+// 4 l16 .. 4 l16 + 3 in v): returns the 4 codes packed low nibble first and
+// the block's absmax in *amax (on every lane of the group).
+template <bool BINNED>
+__device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Midpoints& mp, const BinTables& bt,
+                                                   float* amax) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+  for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+  *amax = a;
+  const double a64 = (double)a;
+  uint32_t c[4];
+  if (!BINNED || a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> the zero code
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = scan_code(v[i], a64, mp);
+  } else {
+    const float inv = __builtin_amdgcn_rcpf(a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int b = (int)((v[i] * inv + 1.0f) * (0.5f * kBins));
+      b = b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
+      const uint32_t cc = bt.code[b];
+      c[i] = ((double)v[i] > a64 * bt.thr[b]) ? (cc >> 8) : (cc & 0xFFu);
+    }
+  }
+  return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
+}
+
+// Stores the 4 codes of elements e0 .. e0 + 3 (n is even: pairs are whole).
+__device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, int64_t n, int64_t e0, uint32_t packed) {
+  if (e0 + 4 <= n) {
+    *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
+  } else {
+    if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);
+    if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+  }
+}
+
+template <typename T, bool BINNED>
+__device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
+                                                float* __restrict__ absmax, const Midpoints& mp) {
+  __shared__ BinTables bt;
+  if (BINNED) {
+    bin_tables_to_lds(bt, mp);
+    __syncthreads();
+  }
   const int64_t nb = (n + kBlock - 1) / kBlock;
   constexpr int G = kQGroupBlocks;
   const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * G;
@@ -101,89 +156,110 @@ __device__ __forceinline__ void quantize_nf4_binned(const T* __restrict__ W, int
   for (int g = 0; g < G; ++g) {
     const int64_t blk = blk0 + g;
     if (blk >= nb) break;  // uniform per 16-lane group
-    const int64_t e0 = blk * kBlock + l16 * 4;
-    float a = fmaxf(fmaxf(fabsf(v[g][0]), fabsf(v[g][1])), fmaxf(fabsf(v[g][2]), fabsf(v[g][3])));
-#pragma unroll
-    for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+    float a;
+    const uint32_t packed = quantize_block<BINNED>(v[g], mp, bt, &a);
     if (l16 == 0) absmax[blk] = a;
-
-    const double a64 = (double)a;
-    uint32_t c[4];
-    if (a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> code 7
-      double thr[15];
-#pragma unroll
-      for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = nf4_code(v[g][i], a64, thr);
-    } else {
-      const float inv = __builtin_amdgcn_rcpf(a);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int b = (int)((v[g][i] * inv + 1.0f) * (0.5f * kBins));
-        b = b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
-        c[i] = s_lo[b] + (((double)v[g][i] > a64 * s_thr[b]) ? 1u : 0u);
-      }
-    }
-    const uint32_t packed = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
-    if (blk * kBlock + kBlock <= n) {
-      *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
-    } else {
-      if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);  // n is even: pairs are whole
-      if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
-    }
+    store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
   }
 }
 
-// One kernel per weight type, so that traces tell them apart.
+// One kernel per weight type and decision flavour, so that traces tell them
+// apart.
 __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
                                                            uint8_t* __restrict__ codes, float* __restrict__ absmax,
                                                            Midpoints mp) {
-  quantize_nf4_binned(W, n, codes, absmax, mp);
+  quantize_blocks<float, true>(W, n, codes, absmax, mp);
 }
 __global__ __launch_bounds__(256) void quantize_nf4_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ absmax, Midpoints mp) {
-  quantize_nf4_binned(W, n, codes, absmax, mp);
+  quantize_blocks<uint16_t, true>(W, n, codes, absmax, mp);
 }
-
-// Exact linear scan over the 15 boundaries (used when the bins above do not
-// separate the boundaries of the codebook in use).
+// Exact linear scan over the boundaries for every weight (types whose
+// boundaries the bins do not separate, e.g. FP4, whose boundary 1/8 lies on
+// a bin edge).
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const T* __restrict__ W, int64_t n,
-                                                           uint8_t* __restrict__ codes,
-                                                           float* __restrict__ absmax, Midpoints mp) {
-  const int64_t nb = (n + kBlock - 1) / kBlock;
-  constexpr int G = kQGroupBlocks;
-  const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * G;
-  const int l16 = threadIdx.x & 15;
-  if (blk0 >= nb) return;  // whole 16-lane groups leave together
-  float v[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g) load_weights4(W, n, (blk0 + g) * kBlock + l16 * 4, v[g]);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int64_t blk = blk0 + g;
-    if (blk >= nb) break;  // uniform per 16-lane group
-    const int64_t e0 = blk * kBlock + l16 * 4;
-    float a = fmaxf(fmaxf(fabsf(v[g][0]), fabsf(v[g][1])), fmaxf(fabsf(v[g][2]), fabsf(v[g][3])));
-#pragma unroll
-    for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
-    if (l16 == 0) absmax[blk] = a;
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ absmax, Midpoints mp) {
+  quantize_blocks<T, false>(W, n, codes, absmax, mp);
+}
 
-    const double a64 = (double)a;
-    double thr[15];
+// ---------------------------------------------------------------------------
+// Fused quantize + double quant: W[n] -> codes[n/2], q8[nb], s2[ceil(nb/256)].
+// One workgroup per group of 256 blocks (16384 weights): four passes of 64
+// blocks quantize the weights as above and keep each block's fp32 absmax in
+// LDS; then thread t turns absmax t into its 8-bit code against the group's
+// maximum.  The absmax values never travel through memory.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t q8_code(float c, double s2d, double scale);
+
+template <typename T, bool BINNED>
+__device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ q8, float* __restrict__ s2,
+                                                  const Midpoints& mp) {
+  __shared__ BinTables bt;
+  __shared__ float s_amax[kBlock2];
+  __shared__ float s_wmax[4];
+  if (BINNED) bin_tables_to_lds(bt, mp);
+  __syncthreads();
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t gblk = (int64_t)blockIdx.x * kBlock2;  // first block of the group
+  const int l16 = threadIdx.x & 15, lg = threadIdx.x >> 4;
+  constexpr int G = kQGroupBlocks;
 #pragma unroll
-    for (int j = 0; j < 15; ++j) thr[j] = a64 * mp.m[j];
-    const uint32_t c0 = nf4_code(v[g][0], a64, thr), c1 = nf4_code(v[g][1], a64, thr);
-    const uint32_t c2 = nf4_code(v[g][2], a64, thr), c3 = nf4_code(v[g][3], a64, thr);
-    const uint32_t packed = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
-    if (blk * kBlock + kBlock <= n) {
-      *reinterpret_cast<uint16_t*>(codes + e0 / 2) = (uint16_t)packed;
-    } else {
-      if (e0 < n) codes[e0 / 2] = (uint8_t)(packed & 0xFF);  // n is even: pairs are whole
-      if (e0 + 2 < n) codes[e0 / 2 + 1] = (uint8_t)(packed >> 8);
+  for (int pass = 0; pass < kBlock2 / (16 * G); ++pass) {
+    const int local0 = pass * 16 * G + lg * G;  // block of the group, 0..255
+    float v[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t blk = gblk + local0 + g;
+      if (blk < nb) load_weights4(W, n, blk * kBlock + l16 * 4, v[g]);
+      else v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t blk = gblk + local0 + g;
+      float a;
+      const uint32_t packed = quantize_block<BINNED>(v[g], mp, bt, &a);  // every lane group takes part
+      if (l16 == 0) s_amax[local0 + g] = a;                                // 0 past the last block
+      if (blk < nb) store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
     }
   }
+  __syncthreads();
+  // s2 = the group's maximum absmax (exact fp32; the zeros past the last
+  // block never raise it), then q8 of block t.
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float c = s_amax[t];
+  float m = c;
+#pragma unroll
+  for (int off = 32; off; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) s_wmax[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+  if (t == 0) s2[blockIdx.x] = m;
+  const double s2d = (double)m;
+  const uint32_t q = m > 0.0f ? q8_code(c, s2d, 255.0 / s2d) : 0u;
+  if (gblk + t < nb) q8[gblk + t] = (uint8_t)q;
+}
+
+__global__ __launch_bounds__(256) void quantize_dq_kernel(const float* __restrict__ W, int64_t n,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
+                                                          float* __restrict__ s2, Midpoints mp) {
+  quantize_dq_group<float, true>(W, n, codes, q8, s2, mp);
+}
+__global__ __launch_bounds__(256) void quantize_dq_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ q8, float* __restrict__ s2,
+                                                               Midpoints mp) {
+  quantize_dq_group<uint16_t, true>(W, n, codes, q8, s2, mp);
+}
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_dq_scan_kernel(const T* __restrict__ W, int64_t n,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ q8, float* __restrict__ s2,
+                                                               Midpoints mp) {
+  quantize_dq_group<T, false>(W, n, codes, q8, s2, mp);
 }
 
 // ---------------------------------------------------------------------------
@@ -280,31 +356,51 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------------------
 namespace {
-template <typename T>
-hipError_t launch_quantize_nf4_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints),
-                                 const T* W, int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp,
-                                 const char* name, hipStream_t s) {
-  const int64_t nb = (n + kBlock - 1) / kBlock;
-  constexpr int G = kQGroupBlocks;
-  const int64_t grid = (nb + 16 * G - 1) / (16 * G);
-  // The bins must hold at most one boundary each, none within 1e-5 of an edge.
-  bool binned = true;
-  for (int b = 0; b < kBins && binned; ++b) {
+// The bins can be used when each holds at most one boundary of the type and
+// none lies within 1e-5 of a bin edge.
+bool bins_separate(const Midpoints& mp) {
+  for (int b = 0; b < kBins; ++b) {
     const double lo = -1.0 + b * (2.0 / kBins), hi = lo + 2.0 / kBins;
     int inside = 0;
     for (int j = 0; j < 15; ++j) {
+      if (!std::isfinite(mp.m[j])) continue;
       if (mp.m[j] >= lo && mp.m[j] < hi) ++inside;
-      if (std::fabs(mp.m[j] - lo) < 1e-5 || std::fabs(mp.m[j] - hi) < 1e-5) binned = false;
+      if (std::fabs(mp.m[j] - lo) < 1e-5 || std::fabs(mp.m[j] - hi) < 1e-5) return false;
     }
-    if (inside > 1) binned = false;
+    if (inside > 1) return false;
   }
-  {
+  return true;
+}
+
+template <typename T>
+hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints), const T* W,
+                             int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp, const char* name,
+                             hipStream_t s) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  constexpr int G = kQGroupBlocks;
+  const int64_t grid = (nb + 16 * G - 1) / (16 * G);
+  if (bins_separate(mp)) {
     KernelTimer kt_(name, s);
-    if (binned)
-      hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
-    else
-      hipLaunchKernelGGL(quantize_nf4_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax,
-                         mp);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+  } else {
+    KernelTimer kt_("quantize_nf4_scan_kernel", s);
+    hipLaunchKernelGGL(quantize_nf4_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, uint8_t*, float*, Midpoints),
+                                const T* W, int64_t n, uint8_t* codes, uint8_t* q8, float* s2, const Midpoints& mp,
+                                const char* name, hipStream_t s) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t grid = (nb + kBlock2 - 1) / kBlock2;
+  if (bins_separate(mp)) {
+    KernelTimer kt_(name, s);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp);
+  } else {
+    KernelTimer kt_("quantize_dq_scan_kernel", s);
+    hipLaunchKernelGGL(quantize_dq_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp);
   }
   return hipGetLastError();
 }
@@ -312,13 +408,21 @@ hipError_t launch_quantize_nf4_t(void (*binned_kernel)(const T*, int64_t, uint8_
 
 hipError_t launch_quantize_nf4(const float* W, int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp,
                                hipStream_t s) {
-  return launch_quantize_nf4_t(quantize_nf4_kernel, W, n, codes, absmax, mp, "quantize_nf4_kernel", s);
+  return launch_quantize_t(quantize_nf4_kernel, W, n, codes, absmax, mp, "quantize_nf4_kernel", s);
 }
 
 hipError_t launch_quantize_nf4_bf16(const uint16_t* W, int64_t n, uint8_t* codes, float* absmax,
                                     const Midpoints& mp, hipStream_t s) {
-  return launch_quantize_nf4_t(quantize_nf4_bf16_kernel, W, n, codes, absmax, mp, "quantize_nf4_bf16_kernel",
-                               s);
+  return launch_quantize_t(quantize_nf4_bf16_kernel, W, n, codes, absmax, mp, "quantize_nf4_bf16_kernel", s);
+}
+
+hipError_t launch_quantize_dq(const void* W, bool bf16, int64_t n, uint8_t* codes, uint8_t* q8, float* s2,
+                              const Midpoints& mp, hipStream_t s) {
+  if (bf16)
+    return launch_quantize_dq_t(quantize_dq_bf16_kernel, static_cast<const uint16_t*>(W), n, codes, q8, s2, mp,
+                                "quantize_dq_bf16_kernel", s);
+  return launch_quantize_dq_t(quantize_dq_kernel, static_cast<const float*>(W), n, codes, q8, s2, mp,
+                              "quantize_dq_kernel", s);
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* q8, float* s2, hipStream_t s) {

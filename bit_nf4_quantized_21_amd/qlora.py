@@ -32,6 +32,18 @@ _SIGNATURES = {
                                                 _c_f, _c_p, _c_p, _c_p]),
     "qlora_linear_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                         _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "qlora_4bit_table": (ctypes.c_int, [_c_i32, ctypes.POINTER(ctypes.c_float)]),
+    "qlora_quantize_4bit": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "qlora_quantize_dq": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+    "qlora_dequantize_4bit": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p]),
+    "qlora_linear_fwd_4bit": (ctypes.c_int, [_c_i32, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                             _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "qlora_linear_bwd_4bit": (ctypes.c_int, [_c_i32, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                             _c_p, _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "qlora_save_4bit": (ctypes.c_int, [ctypes.c_char_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "qlora_load_4bit_info": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64),
+                                            ctypes.POINTER(_c_i64)]),
+    "qlora_load_4bit": (ctypes.c_int, [ctypes.c_char_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "qlora_timing_enable": (None, [ctypes.c_int]),
     "qlora_timing_read": (ctypes.c_int, [ctypes.c_char_p, _c_sz]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -39,6 +51,15 @@ _SIGNATURES = {
     "qlora_last_hip_error": (ctypes.c_int, []),
     "qlora_device_status": (ctypes.c_int, [_c_p]),
 }
+
+
+QTYPES = {"nf4": 0, "int4": 1, "fp4": 2}
+
+
+def _qtype(qtype):
+    if qtype not in QTYPES:
+        raise ValueError(f"qtype must be one of {sorted(QTYPES)}")
+    return QTYPES[qtype]
 
 
 def lib():
@@ -145,8 +166,16 @@ def nf4_codebook():
     return [buf[i] for i in range(16)]
 
 
-def quantize_nf4(W, codes=None, absmax=None, stream=None):
-    """W: fp32 or bf16 CUDA tensor (flattened row-major).  Returns (codes u8, absmax f32)."""
+def table_4bit(qtype="nf4"):
+    """The library's 16 fp32 decode values of a stored 4-bit type, by code."""
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qlora_4bit_table(_qtype(qtype), buf))
+    return [buf[i] for i in range(16)]
+
+
+def quantize_nf4(W, codes=None, absmax=None, stream=None, qtype="nf4"):
+    """W: fp32 or bf16 CUDA tensor (flattened row-major).  Returns (codes u8,
+    absmax f32).  qtype selects the stored 4-bit type (nf4, int4, fp4)."""
     torch = _torch()
     bf16 = W.dtype == torch.bfloat16
     _dev(W, torch.bfloat16 if bf16 else torch.float32, "W")
@@ -154,13 +183,31 @@ def quantize_nf4(W, codes=None, absmax=None, stream=None):
     nb = (n + 63) // 64
     codes = torch.empty(n // 2, dtype=torch.uint8, device=W.device) if codes is None else codes
     absmax = torch.empty(nb, dtype=torch.float32, device=W.device) if absmax is None else absmax
-    _dev(codes, torch.uint8, "codes")
-    _dev(absmax, torch.float32, "absmax")
-    if codes.numel() < n // 2 or absmax.numel() < nb:
-        raise ValueError("output buffers too small")
-    entry = lib().qlora_quantize_nf4_bf16 if bf16 else lib().qlora_quantize_nf4
-    _check(entry(_p(W), n, 64, _p(codes), _p(absmax), _stream(stream)))
+    _need(_dev(codes, torch.uint8, "codes"), n // 2, "codes")
+    _need(_dev(absmax, torch.float32, "absmax"), nb, "absmax")
+    _check(lib().qlora_quantize_4bit(_p(W), 1 if bf16 else 0, n, 64, _qtype(qtype), _p(codes), _p(absmax),
+                                     _stream(stream)))
     return codes, absmax
+
+
+def quantize_dq(W, qtype="nf4", codes=None, q8=None, s2=None, stream=None):
+    """Quantization and double quantization in one pass.  Returns (codes u8,
+    q8 u8, s2 f32), bit-identical to quantize_nf4 followed by double_quant."""
+    torch = _torch()
+    bf16 = W.dtype == torch.bfloat16
+    _dev(W, torch.bfloat16 if bf16 else torch.float32, "W")
+    n = W.numel()
+    nb = (n + 63) // 64
+    ng = (nb + 255) // 256
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=W.device) if codes is None else codes
+    q8 = torch.empty(nb, dtype=torch.uint8, device=W.device) if q8 is None else q8
+    s2 = torch.empty(ng, dtype=torch.float32, device=W.device) if s2 is None else s2
+    _need(_dev(codes, torch.uint8, "codes"), n // 2, "codes")
+    _need(_dev(q8, torch.uint8, "q8"), nb, "q8")
+    _need(_dev(s2, torch.float32, "s2"), ng, "s2")
+    _check(lib().qlora_quantize_dq(_p(W), 1 if bf16 else 0, n, _qtype(qtype), _p(codes), _p(q8), _p(s2),
+                                   _stream(stream)))
+    return codes, q8, s2
 
 
 def double_quant(absmax, q8=None, s2=None, stream=None):
@@ -179,7 +226,7 @@ def double_quant(absmax, q8=None, s2=None, stream=None):
     return q8, s2
 
 
-def dequantize_nf4(codes, q8, s2, n, dtype=None, out=None, stream=None):
+def dequantize_nf4(codes, q8, s2, n, dtype=None, out=None, stream=None, qtype="nf4"):
     """Dense weight from NF4 + double-quant storage; bf16 (default) or fp32."""
     torch = _torch()
     dtype = torch.bfloat16 if dtype is None else dtype
@@ -194,8 +241,8 @@ def dequantize_nf4(codes, q8, s2, n, dtype=None, out=None, stream=None):
     _need(q8, (n + 63) // 64, "q8")
     _need(s2, ((n + 63) // 64 + 255) // 256, "s2")
     _need(out, n, "out")
-    _check(lib().qlora_dequantize_nf4(_p(codes), _p(q8), _p(s2), n, 1 if dtype == torch.bfloat16 else 0,
-                                      _p(out), _stream(stream)))
+    _check(lib().qlora_dequantize_4bit(_p(codes), _p(q8), _p(s2), n, _qtype(qtype),
+                                       1 if dtype == torch.bfloat16 else 0, _p(out), _stream(stream)))
     return out
 
 
@@ -221,7 +268,7 @@ def _workspace(nbytes, device, ws):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None, stream=None):
+def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None, stream=None, qtype="nf4"):
     """Y = X W'^T + (alpha/r) (X A) B and XA = X A.  Returns (Y bf16 [T,N], XA f32 [T,r])."""
     torch = _torch()
     _dev(X, torch.bfloat16, "X")
@@ -241,8 +288,8 @@ def linear_fwd(X, codes, q8, s2, A, B, alpha, N, Y=None, XA=None, workspace=None
     _need(_dev(XA, torch.float32, "XA"), T * r, "XA")
     nbytes = linear_fwd_workspace_bytes(T, K, N, r)
     workspace = _workspace(nbytes, X.device, workspace)
-    _check(lib().qlora_linear_fwd(_p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r, float(alpha),
-                                  _p(Y), _p(XA), _p(workspace), nbytes, _stream(stream)))
+    _check(lib().qlora_linear_fwd_4bit(_qtype(qtype), _p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r,
+                                       float(alpha), _p(Y), _p(XA), _p(workspace), nbytes, _stream(stream)))
     return Y, XA
 
 
@@ -268,7 +315,8 @@ def linear_fwd_noalloc(X, codes, q8, s2, A, B, alpha, N, Y, XA, stream=None):
     return Y, XA
 
 
-def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None, workspace=None, stream=None):
+def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None, workspace=None, stream=None,
+               qtype="nf4"):
     """Returns (dX bf16 [T,K], dA bf16 [K,r], dB bf16 [r,N])."""
     torch = _torch()
     _dev(dY, torch.bfloat16, "dY")
@@ -292,6 +340,39 @@ def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None,
         _need(_dev(t, torch.bfloat16, nm), n, nm)
     nbytes = linear_bwd_workspace_bytes(T, K, N, r)
     workspace = _workspace(nbytes, X.device, workspace)
-    _check(lib().qlora_linear_bwd(_p(dY), _p(X), _p(XA), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r,
-                                  float(alpha), _p(dX), _p(dA), _p(dB), _p(workspace), nbytes, _stream(stream)))
+    _check(lib().qlora_linear_bwd_4bit(_qtype(qtype), _p(dY), _p(X), _p(XA), T, K, N, _p(codes), _p(q8), _p(s2),
+                                       _p(A), _p(B), r, float(alpha), _p(dX), _p(dA), _p(dB), _p(workspace), nbytes,
+                                       _stream(stream)))
     return dX, dA, dB
+
+
+def save_4bit(path, codes, q8, s2, N, K, qtype="nf4", stream=None):
+    """Write a quantized N x K weight to a safetensors file (host-blocking)."""
+    torch = _torch()
+    _dev(codes, torch.uint8, "codes")
+    _dev(q8, torch.uint8, "q8")
+    _dev(s2, torch.float32, "s2")
+    _weight(codes, q8, s2, N, K)
+    _check(lib().qlora_save_4bit(os.fsencode(path), _qtype(qtype), N, K, _p(codes), _p(q8), _p(s2),
+                                 _stream(stream)))
+
+
+def load_4bit_info(path):
+    """(qtype name, N, K) of a saved weight."""
+    q, n, k = _c_i32(), _c_i64(), _c_i64()
+    _check(lib().qlora_load_4bit_info(os.fsencode(path), ctypes.byref(q), ctypes.byref(n), ctypes.byref(k)))
+    name = {v: key for key, v in QTYPES.items()}[q.value]
+    return name, n.value, k.value
+
+
+def load_4bit(path, device="cuda", stream=None):
+    """Read a saved weight into new device tensors: (codes, q8, s2, qtype, N, K)."""
+    torch = _torch()
+    qtype, N, K = load_4bit_info(path)
+    nb = (N * K + 63) // 64
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=device)
+    q8 = torch.empty(nb, dtype=torch.uint8, device=device)
+    s2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=device)
+    _check(lib().qlora_load_4bit(os.fsencode(path), _qtype(qtype), N, K, _p(codes), _p(q8), _p(s2),
+                                 _stream(stream)))
+    return codes, q8, s2, qtype, N, K

@@ -54,8 +54,33 @@ typedef enum {
   QLORA_ERR_HIP = -5,         /* a HIP launch or query failed; see qlora_last_hip_error() */
   QLORA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
   QLORA_ERR_DEVICE = -7,      /* a kernel's bounded wait ran out (reported by qlora_device_status) */
-  QLORA_ERR_SCRATCH = -8      /* the problem needs more than the no-allocation entry point's scratch */
+  QLORA_ERR_SCRATCH = -8,     /* the problem needs more than the no-allocation entry point's scratch */
+  QLORA_ERR_IO = -9           /* a file is missing, unreadable, malformed, or of another type or shape */
 } qlora_status;
+
+/*
+ * Stored 4-bit types.  NF4 is the type QLoRA introduces (Abstract item (a));
+ * Int4 and FP4 are the 4-bit integer and float types the pages compare it
+ * with (news write-up, innovations list: NF4 gives better results than
+ * 4-bit integers and 4-bit floats).  Each is a 16-entry fp32 decode table
+ * (qlora_4bit_table); quantization, double quantization, dequantization and
+ * the linear layer are the same for all three with the type's table:
+ *   NF4   the codebook described at qlora_quantize_nf4;
+ *   INT4  code = k mod 16 (4-bit two's complement), value fp32(k/7),
+ *         k = -7..7 (symmetric absmax); code 8 is never produced;
+ *   FP4   OCP E2M1: code = sign<<3 | exponent<<1 | mantissa (bias 1,
+ *         subnormal at exponent 0), value (-1)^sign * fp32(m/6) for the
+ *         magnitudes m = 0, 0.5, 1, 1.5, 2, 3, 4, 6; code 8 (-0) is never
+ *         produced.
+ * The code of a weight is that of the type's level nearest to w/absmax in
+ * exact arithmetic (ties to the lower level); an all-zero block gets the
+ * code of 0.
+ */
+typedef enum { QLORA_QTYPE_NF4 = 0, QLORA_QTYPE_INT4 = 1, QLORA_QTYPE_FP4 = 2 } qlora_qtype;
+
+/* Host: the 16 fp32 decode values of a type, indexed by code.  Returns
+ * QLORA_ERR_UNSUPPORTED for an unknown type, QLORA_ERR_NULL for out = NULL. */
+int qlora_4bit_table(int32_t qtype, float out[16]);
 
 /*
  * Blockwise NF4 quantization (Abstract item (a); innovations list, NF4).
@@ -89,6 +114,29 @@ int qlora_quantize_nf4(const float* W, int64_t n, int32_t blocksize,
  */
 int qlora_quantize_nf4_bf16(const uint16_t* W, int64_t n, int32_t blocksize,
                             uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * Blockwise quantization to any stored 4-bit type (see qlora_qtype).
+ *   W          [n] fp32 (w_is_bf16 = 0) or bf16 bits (w_is_bf16 = 1).
+ *   Other arguments, outputs and errors as qlora_quantize_nf4; qtype must be
+ *   a qlora_qtype (else QLORA_ERR_UNSUPPORTED).
+ */
+int qlora_quantize_4bit(const void* W, int32_t w_is_bf16, int64_t n, int32_t blocksize, int32_t qtype,
+                        uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * Quantization and double quantization in one pass (Abstract items (a) and
+ * (b)): the same codes, q8 and s2 as qlora_quantize_4bit followed by
+ * qlora_double_quant, bit for bit, without writing or re-reading the fp32
+ * absmax constants (each group of 256 blocks keeps them on chip).
+ *   W      [n]              fp32 (w_is_bf16 = 0) or bf16 bits (w_is_bf16 = 1).
+ *   n                       even, >= 0 (0 = no-op).  Block sizes are 64 and 256.
+ *   codes  [n/2]            out, as qlora_quantize_4bit.
+ *   q8     [ceil(n/64)]     out, as qlora_double_quant.
+ *   s2     [ceil(n/16384)]  out, as qlora_double_quant.
+ */
+int qlora_quantize_dq(const void* W, int32_t w_is_bf16, int64_t n, int32_t qtype,
+                      uint8_t* codes, uint8_t* q8, float* s2, void* stream);
 
 /*
  * Double quantization of the absmax constants (Abstract item (b);
@@ -203,6 +251,48 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA,
  */
 int qlora_dequantize_nf4(const uint8_t* codes, const uint8_t* q8, const float* s2,
                          int64_t n, int32_t out_is_bf16, void* out, void* stream);
+
+/* Dequantization for any stored type (as qlora_dequantize_nf4 with the
+ * type's table). */
+int qlora_dequantize_4bit(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t n, int32_t qtype,
+                          int32_t out_is_bf16, void* out, void* stream);
+
+/*
+ * The linear layer with a base weight of any stored 4-bit type: exactly
+ * qlora_linear_fwd / qlora_linear_bwd (same arguments after qtype, same
+ * kernels, results and errors) with W' = bf16(table[code] * c1').
+ */
+int qlora_linear_fwd_4bit(int32_t qtype, const uint16_t* X, int64_t T, int64_t K, int64_t N,
+                          const uint8_t* codes, const uint8_t* q8, const float* s2,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                          uint16_t* Y, float* XA, void* workspace, size_t workspace_bytes, void* stream);
+int qlora_linear_bwd_4bit(int32_t qtype, const uint16_t* dY, const uint16_t* X, const float* XA,
+                          int64_t T, int64_t K, int64_t N,
+                          const uint8_t* codes, const uint8_t* q8, const float* s2,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                          uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Storage of a quantized weight (the format is deterministic, so a saved
+ * weight reloads bit for bit).  The file is a safetensors file: tensors
+ * "s2" (F32 [ceil(N*K/16384)]), "codes" (U8 [N*K/2]) and "q8"
+ * (U8 [ceil(N*K/64)]), and metadata naming the format ("qlora-4bit"), the
+ * type ("nf4", "int4", "fp4"), N, K, the block sizes (64, 256) and the
+ * type's decode table as fp32 bit patterns.  These calls wait for `stream`
+ * and copy through host memory (they are host-blocking, unlike the others).
+ *   qlora_save_4bit       writes the device buffers of an N x K weight.
+ *   qlora_load_4bit_info  reads a file's type, N and K (no device access).
+ *   qlora_load_4bit       checks that the file holds exactly this type,
+ *                         N and K and this library's decode table, then
+ *                         copies the tensors into the device buffers.
+ * File errors and any mismatch return QLORA_ERR_IO.
+ */
+int qlora_save_4bit(const char* path, int32_t qtype, int64_t N, int64_t K,
+                    const uint8_t* codes, const uint8_t* q8, const float* s2, void* stream);
+int qlora_load_4bit_info(const char* path, int32_t* qtype, int64_t* N, int64_t* K);
+int qlora_load_4bit(const char* path, int32_t qtype, int64_t N, int64_t K,
+                    uint8_t* codes, uint8_t* q8, float* s2, void* stream);
 
 /*
  * Support: per-kernel timing for benchmarks.  While enabled, every kernel the

@@ -144,3 +144,62 @@ def test_binding_checks_buffer_sizes():
     with pytest.raises(ValueError):
         qlora._weight(torch.empty(10, dtype=torch.uint8), torch.empty(1, dtype=torch.uint8),
                       torch.empty(1), 8, 64)
+
+
+def test_type_tables_match_oracle_bitwise(L):
+    from oracle import baselines
+    for name, q in qlora.QTYPES.items():
+        got = np.array(qlora.table_4bit(name), dtype=np.float32)
+        assert np.array_equal(got.view(np.uint32), baselines.type_table(name).view(np.uint32)), name
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_4bit_table(3, buf) == EUNSUP
+    assert L.qlora_4bit_table(0, None) == ENULL
+
+
+def test_4bit_entry_point_argument_errors(L):
+    assert L.qlora_quantize_4bit(P, 0, 128, 64, 3, P, P, None) == EUNSUP     # unknown type
+    assert L.qlora_quantize_4bit(P, 2, 128, 64, 0, P, P, None) == EUNSUP     # w_is_bf16 not 0/1
+    assert L.qlora_quantize_4bit(P, 0, 127, 64, 1, P, P, None) == ESHAPE
+    assert L.qlora_quantize_4bit(P, 1, 128, 64, 2, P, None, None) == ENULL
+    assert L.qlora_quantize_4bit(MIS, 0, 128, 64, 2, P, P, None) == EALIGN
+    assert L.qlora_quantize_dq(P, 0, 128, -1, P, P, P, None) == EUNSUP
+    assert L.qlora_quantize_dq(P, 0, 127, 0, P, P, P, None) == ESHAPE
+    assert L.qlora_quantize_dq(P, 0, 128, 0, P, None, P, None) == ENULL
+    assert L.qlora_quantize_dq(P, 0, 128, 0, P, P, MIS, None) == EALIGN
+    assert L.qlora_quantize_dq(None, 0, 0, 0, None, None, None, None) == OK
+    assert L.qlora_dequantize_4bit(P, P, P, 64, 5, 1, P, None) == EUNSUP
+    assert L.qlora_dequantize_4bit(P, P, P, 64, 1, 3, P, None) == EUNSUP
+    fwd = L.qlora_linear_fwd_4bit(7, P, 4, 128, 64, P, P, P, P, P, 8, 16.0, P, P, P, 1 << 30, None)
+    assert fwd == EUNSUP
+    bwd = L.qlora_linear_bwd_4bit(-1, P, P, P, 4, 128, 64, P, P, P, P, P, 8, 16.0, P, P, P, P, 1 << 30, None)
+    assert bwd == EUNSUP
+
+
+def test_load_info_reads_a_safetensors_header(tmp_path):
+    """A file written by the independent safetensors package in the library's
+    layout is understood by the header reader (no device access); malformed
+    or foreign files are refused with QLORA_ERR_IO."""
+    st = pytest.importorskip("safetensors.numpy")
+    from oracle import baselines
+    N, K = 16, 128
+    nb = N * K // 64
+    table = ",".join(f"{int(u):08x}" for u in baselines.type_table("fp4").view(np.uint32))
+    meta = {"format": "qlora-4bit", "qtype": "fp4", "N": str(N), "K": str(K), "blocksize": "64",
+            "blocksize2": "256", "table": table}
+    tensors = {"s2": np.zeros(1, np.float32), "codes": np.zeros(N * K // 2, np.uint8), "q8": np.zeros(nb, np.uint8)}
+    good = tmp_path / "w.safetensors"
+    st.save_file(tensors, str(good), metadata=meta)
+    assert qlora.load_4bit_info(str(good)) == ("fp4", N, K)
+    bad = tmp_path / "bad.safetensors"
+    st.save_file(tensors, str(bad), metadata=dict(meta, table=table.replace("3daaaaab", "3daaaaac")))
+    with pytest.raises(qlora.QLoRAError):
+        qlora.load_4bit_info(str(bad))
+    short = tmp_path / "short.safetensors"
+    st.save_file({**tensors, "q8": np.zeros(nb - 1, np.uint8)}, str(short), metadata=meta)
+    with pytest.raises(qlora.QLoRAError):
+        qlora.load_4bit_info(str(short))
+    (tmp_path / "junk").write_bytes(b"\x10\x00\x00\x00\x00\x00\x00\x00{not json at all}")
+    with pytest.raises(qlora.QLoRAError):
+        qlora.load_4bit_info(str(tmp_path / "junk"))
+    with pytest.raises(qlora.QLoRAError):
+        qlora.load_4bit_info(str(tmp_path / "missing"))
