@@ -125,8 +125,6 @@ def quantize_all(torch, qlora, synth, wl, lins):
     per_layer = len(wl.linears)
     layer_elems = sum(l.N * l.K for l in wl.linears)
     buf = torch.empty(layer_elems, dtype=torch.float32, device="cuda")
-    max_nb = max(l.N * l.K // 64 for l in wl.linears)
-    absmax = torch.empty(max_nb, dtype=torch.float32, device="cuda")
     weights = []
     qlora.timing_read()
     for layer in range(wl.layers):
@@ -143,21 +141,21 @@ def quantize_all(torch, qlora, synth, wl, lins):
             codes = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
             q8 = torch.empty(n // 64, dtype=torch.uint8, device="cuda")
             s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device="cuda")
-            qlora.quantize_nf4(v, codes, absmax[: n // 64])
-            qlora.double_quant(absmax[: n // 64], q8, s2)
+            qlora.quantize_dq(v, "nf4", codes, q8, s2)   # quantize + double quant in one pass
             weights.append((codes, q8, s2))
         qlora.timing_enable(False)
     torch.cuda.synchronize()
     kt = qlora.timing_read()
-    del buf, absmax
+    del buf
     torch.cuda.empty_cache()
     params = sum(N * K for (_, _, N, K) in lins)
     ms = sum(t for (_, t) in kt.values())
-    # algorithmic bytes: fp32 weights read once; codes, absmax written and
-    # absmax read back by the double quantization; q8 and s2 written
+    # algorithmic bytes of the one-pass kernel: fp32 weights read once;
+    # codes, q8 and s2 written once
     nb = params // 64
-    alg = 4 * params + params // 2 + 4 * nb + 4 * nb + nb + 4 * ((nb + 255) // 256)
-    res = {"workload": f"{wl.name}: quantize all {len(lins)} linears from fp32 (blockwise NF4 + double quant)",
+    alg = 4 * params + params // 2 + nb + 4 * ((nb + 255) // 256)
+    res = {"workload": f"{wl.name}: quantize all {len(lins)} linears from fp32 (blockwise NF4 + double quant in "
+                       "one pass)",
            "params": params, "kernel_ms": round(ms, 3),
            "kernels": {k: {"launches": n, "total_ms": round(t, 3)} for k, (n, t) in kt.items()},
            "algorithmic_bytes": alg, "GBs": round(alg / (ms * 1e-3) / 1e9, 1),
@@ -167,30 +165,51 @@ def quantize_all(torch, qlora, synth, wl, lins):
     return weights, res
 
 
+# Linears of a layer that take the same input in a LLaMA block and have the
+# same shape run as one batched launch (the layer's other linears alone).
+FUSED_SETS = ({"q_proj", "k_proj", "v_proj"}, {"gate_proj", "up_proj"})
+
+
 def make_linears(torch, qlora, synth, wl, lins, weights):
-    """Per-linear inputs and gradients; shared Y / dX outputs and workspaces."""
+    """Per-linear inputs and gradients; shared Y / dX outputs and workspaces;
+    `groups`: the launch groups of the step in layer order."""
     T, r = wl.T, wl.r
     Ls = []
     for (i, name, N, K), (codes, q8, s2) in zip(lins, weights):
         inp = synth.device_inputs(T, N, K, r, i, backward=True, weight=False)
-        L = dict(T=T, N=N, K=K, r=r, codes=codes, q8=q8, s2=s2, **inp)
+        L = dict(T=T, N=N, K=K, r=r, name=name, codes=codes, q8=q8, s2=s2, **inp)
         L["XA"] = torch.empty(T, r, dtype=torch.float32, device="cuda")
         L["dA"] = torch.empty(K, r, dtype=torch.bfloat16, device="cuda")
         L["dB"] = torch.empty(r, N, dtype=torch.bfloat16, device="cuda")
         Ls.append(L)
+    # batched launches write their linears' outputs at once: one Y / dX
+    # buffer per member position of a group
+    groups, cur = [], []
+    for L in Ls:
+        if cur and any(L["name"] in fs and cur[0]["name"] in fs for fs in FUSED_SETS) and \
+                (L["N"], L["K"]) == (cur[0]["N"], cur[0]["K"]):
+            cur.append(L)
+        else:
+            if cur:
+                groups.append(cur)
+            cur = [L]
+    groups.append(cur)
+    width = max(len(g) for g in groups)
     maxN = max(L["N"] for L in Ls)
     maxK = max(L["K"] for L in Ls)
-    Ybuf = torch.empty(T * maxN, dtype=torch.bfloat16, device="cuda")
-    dXbuf = torch.empty(T * maxK, dtype=torch.bfloat16, device="cuda")
-    wsf = max(qlora.linear_fwd_workspace_bytes(T, L["K"], L["N"], r) for L in Ls)
-    wsb = max(qlora.linear_bwd_workspace_bytes(T, L["K"], L["N"], r) for L in Ls)
+    Ybuf = [torch.empty(T * maxN, dtype=torch.bfloat16, device="cuda") for _ in range(width)]
+    dXbuf = [torch.empty(T * maxK, dtype=torch.bfloat16, device="cuda") for _ in range(width)]
+    shapes = {tuple((L["K"], L["N"]) for L in g) for g in groups}
+    wsf = max(qlora.grouped_workspace_bytes(list(sh), T, r) for sh in shapes)
+    wsb = max(qlora.grouped_workspace_bytes(list(sh), T, r, backward=True) for sh in shapes)
     wsf = torch.empty(max(1, wsf), dtype=torch.uint8, device="cuda")
     wsb = torch.empty(max(1, wsb), dtype=torch.uint8, device="cuda")
-    for L in Ls:
-        L["Y"] = Ybuf[: T * L["N"]].view(T, L["N"])
-        L["dX"] = dXbuf[: T * L["K"]].view(T, L["K"])
-        L["wsf"], L["wsb"] = wsf, wsb
-    return Ls
+    for g in groups:
+        for j, L in enumerate(g):
+            L["Y"] = Ybuf[j][: T * L["N"]].view(T, L["N"])
+            L["dX"] = dXbuf[j][: T * L["K"]].view(T, L["K"])
+            L["wsf"], L["wsb"] = wsf, wsb
+    return Ls, groups
 
 
 def run_fwd(qlora, L, alpha):
@@ -203,16 +222,30 @@ def run_bwd(qlora, L, alpha):
                      dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
 
 
-def time_steps(torch, qlora, wl, Ls, steps, warmup, event_steps):
+def run_group_fwd(qlora, g, alpha):
+    if len(g) == 1:
+        run_fwd(qlora, g[0], alpha)
+    else:
+        qlora.linear_fwd_grouped(g, alpha, g[0]["T"], g[0]["r"], workspace=g[0]["wsf"])
+
+
+def run_group_bwd(qlora, g, alpha):
+    if len(g) == 1:
+        run_bwd(qlora, g[0], alpha)
+    else:
+        qlora.linear_bwd_grouped(g, alpha, g[0]["T"], g[0]["r"], workspace=g[0]["wsb"])
+
+
+def time_steps(torch, qlora, wl, Ls, groups, steps, warmup, event_steps):
     """Wall time per step of the fwd (layer order) + bwd (reverse order) step,
     then per-kernel event times from a second pass of event_steps steps."""
     alpha = wl.alpha
 
     def step():
-        for L in Ls:
-            run_fwd(qlora, L, alpha)
-        for L in reversed(Ls):
-            run_bwd(qlora, L, alpha)
+        for g in groups:
+            run_group_fwd(qlora, g, alpha)
+        for g in reversed(groups):
+            run_group_bwd(qlora, g, alpha)
 
     for _ in range(warmup):
         step()
@@ -241,11 +274,12 @@ def time_steps(torch, qlora, wl, Ls, steps, warmup, event_steps):
     roof = None
     if all(f is not None for f in per_step):
         achieved = sum(per_step) * event_steps / (total_ms * 1e-3) / 1e12
+        launches_per_step = launches // event_steps
         roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_from_profiles(name, WORKLOAD_TAG.get(wl.name, wl.name)),
                 "avg_launch_us": round(total_ms * 1e3 / launches, 2), "launches": launches,
-                "algorithmic_flop_per_launch": round(sum(per_step) / len(per_step)),
+                "algorithmic_flop_per_launch": round(sum(per_step) / launches_per_step),
                 "events_pass_ms_per_step": round((t3 - t2) * 1e3 / event_steps, 4)}
     tot = sum(v[1] for v in kt.values())
     kernels = {k: {"launches": n, "avg_us": round(t * 1e3 / n, 2), "share": round(t / tot, 4)}
@@ -261,16 +295,17 @@ def bench_workload(torch, qlora, synth, key, steps, warmup, event_steps=2):
     wl = synth.WORKLOADS[key]
     lins = linear_list(wl)
     weights, qres = quantize_all(torch, qlora, synth, wl, lins)
-    Ls = make_linears(torch, qlora, synth, wl, lins, weights)
+    Ls, groups = make_linears(torch, qlora, synth, wl, lins, weights)
     del weights
-    ms, flops, roof, kernels = time_steps(torch, qlora, wl, Ls, steps, warmup, event_steps)
+    ms, flops, roof, kernels = time_steps(torch, qlora, wl, Ls, groups, steps, warmup, event_steps)
     value = flops / (ms * 1e-3) / 1e12
     res = {"workload": wl.name, "tokens": wl.T, "r": wl.r, "alpha": wl.alpha, "layers": wl.layers,
+           "launch_groups": [[L["name"] for L in g] for g in groups[:len(wl.linears)]],
            "linears": [[l.name, l.N, l.K] for l in wl.linears], "flop_per_step": flops,
            "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
            "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4), "roofline": roof, "kernels": kernels,
            "quantize_all": qres}
-    del Ls
+    del Ls, groups
     torch.cuda.empty_cache()
     return res
 
@@ -330,6 +365,64 @@ def bench_gemv(torch, qlora, synth, copies=48, iters=240):
     return res
 
 
+def bench_gemv_grouped(torch, qlora, synth, copies=4, iters=40, T=4):
+    """The grouped small-token forward over all seven linears of a LLaMA-7B
+    layer (q, k, v, o 4096x4096; gate, up 4096->11008; down 11008->4096; 4
+    tokens, r=64) in one call, rotating over 4 layer copies (415 MB of codes,
+    cold HBM)."""
+    r, alpha = 64, 16.0
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+    groups = []
+    for c in range(copies):
+        layer = []
+        for j, (N, K) in enumerate(shapes):
+            i = 7 * c + j
+            W = torch.empty(N * K, dtype=torch.float32, device="cuda")
+            synth.device_weight(W, i)
+            codes, q8, s2 = qlora.quantize_dq(W)
+            del W
+            inp = synth.device_inputs(T, N, K, r, i, backward=False, weight=False)
+            layer.append(dict(X=inp["X"], A=inp["A"], B=inp["B"], codes=codes, q8=q8, s2=s2,
+                              Y=torch.empty(T, N, dtype=torch.bfloat16, device="cuda"),
+                              XA=torch.empty(T, r, dtype=torch.float32, device="cuda")))
+        groups.append(layer)
+    ws = None
+    for g in groups * 2:
+        qlora.linear_fwd_grouped(g, alpha, T, r, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(iters):
+        qlora.linear_fwd_grouped(groups[i % copies], alpha, T, r)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qlora.timing_read()
+    qlora.timing_enable(True)
+    for i in range(iters):
+        qlora.linear_fwd_grouped(groups[i % copies], alpha, T, r)
+    torch.cuda.synchronize()
+    qlora.timing_enable(False)
+    kt = qlora.timing_read()
+    n, total = kt["gemv_fwd_kernel"]
+    us = total * 1e3 / n
+    kb = sum(gemv_kernel_bytes(T, N, K, r) for (N, K) in shapes)
+    gbs = kb / (us * 1e-6) / 1e9
+    path_us = sum(t for (_, t) in kt.values()) * 1e3 / iters
+    path_bytes = sum(gemv_path_bytes(T, N, K, r) for (N, K) in shapes)
+    res = {"workload": f"llama7b-layer-grouped-gemv-T{T}-r64 (7 linears, 202M NF4+DQ weights, one call)",
+           "value": round(gbs, 1), "unit": "GB/s",
+           "roofline": {"kernel": "gemv_fwd_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "avg_launch_us": round(us, 3), "bytes_per_launch": kb},
+           "fwd_path_us_gpu": round(path_us, 3),
+           "fwd_path_GBs_gpu": round(path_bytes / (path_us * 1e-6) / 1e9, 1),
+           "call_us_wall": round((t1 - t0) * 1e6 / iters, 3),
+           "kernels_avg_us": {k: round(t * 1e3 / c, 3) for k, (c, t) in kt.items()},
+           "layer_copies": copies, "codes_bytes_rotated": copies * sum(dq_bytes(N, K) for (N, K) in shapes)}
+    del groups
+    torch.cuda.empty_cache()
+    return res
+
+
 def _event_median(torch, fn, items, reps):
     """Median over reps calls of fn(item) (items rotated) of the per-call
     event time on the current stream, in microseconds."""
@@ -363,6 +456,13 @@ def bench_quantize(torch, qlora, copies=40, reps=80):
         qlora.quantize_nf4(x, codes, absmax)
     q_us = _event_median(torch, lambda x: qlora.quantize_nf4(x, codes, absmax), srcs, reps)
     d_us = _event_median(torch, lambda a: qlora.double_quant(a, q8, s2), absmaxes, reps)
+    f_us = _event_median(torch, lambda x: qlora.quantize_dq(x, "nf4", codes, q8, s2), srcs, reps)
+    types = {}
+    for kind in ("int4", "fp4"):
+        t_us = _event_median(torch, lambda x: qlora.quantize_dq(x, kind, codes, q8, s2), srcs, reps)
+        fb = 4 * n + n // 2 + nb + 4 * ((nb + 255) // 256)
+        types[kind] = {"median_us": round(t_us, 2), "GBs": round(fb / (t_us * 1e-6) / 1e9, 1),
+                       "frac_hbm": round(fb / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     qbytes = 4 * n + n // 2 + 4 * nb
     dbytes = 4 * nb + nb + 4 * ((nb + 255) // 256)
     res = {"workload": "quantize 11008x4096 -> NF4 + double quant, 40 rotating source copies",
@@ -370,7 +470,13 @@ def bench_quantize(torch, qlora, copies=40, reps=80):
            "quantize_fp32": {"median_us": round(q_us, 2), "GBs": round(qbytes / (q_us * 1e-6) / 1e9, 1),
                              "frac_hbm": round(qbytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": qbytes},
            "double_quant": {"median_us": round(d_us, 2), "GBs": round(dbytes / (d_us * 1e-6) / 1e9, 1),
-                            "bytes": dbytes, "note": "absmax input of 2.8 MB (a warm-cache size by nature)"}}
+                            "bytes": dbytes, "note": "absmax input of 2.8 MB (a warm-cache size by nature)"},
+           "quantize_dq_fused": {"median_us": round(f_us, 2),
+                                 "GBs": round((4 * n + n // 2 + nb + 4 * ((nb + 255) // 256)) / (f_us * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round((4 * n + n // 2 + nb + 4 * ((nb + 255) // 256)) / (f_us * 1e-6)
+                                                   / 1e9 / PEAK_HBM_GBS, 4),
+                                 "bytes": 4 * n + n // 2 + nb + 4 * ((nb + 255) // 256)},
+           "quantize_dq_fused_other_types": types}
     srcs = [x.to(torch.bfloat16) for x in srcs]
     torch.cuda.empty_cache()
     for x in srcs:
@@ -497,6 +603,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="headline workload only (no other workloads, GEMV, quantize or peak probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="workloads,gemv,gemv_grouped,quantize,peaks",
+                    help="extra legs to run after the headline (comma list)")
+    ap.add_argument("--skip-headline", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -509,24 +618,29 @@ def main():
     qlora.lib()
     torch.cuda.set_device(0)
 
-    print(f"bench: {args.workload} set-up", file=sys.stderr, flush=True)
-    head = bench_workload(torch, qlora, synth, args.workload, args.steps, args.warmup)
-    value = head["value"]
-    out = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": head["workload"] + " (NF4 + double quant base resident in HBM, LoRA fwd+bwd on "
-                               "every linear)",
-                   "tokens": head["tokens"], "r": head["r"], "alpha": head["alpha"], "layers": head["layers"],
-                   "linears": head["linears"], "parallelism": "single GPU", "flop_per_step": head["flop_per_step"]},
-        "frac_of_bf16_peak": head["frac_of_bf16_peak"],
-        "roofline": head["roofline"],
-        "kernels": head["kernels"],
-        "quantize_all": head["quantize_all"],
-    }
-    print(f"bench: {args.workload} {value} TFLOP/s", file=sys.stderr, flush=True)
-    if not args.no_extras:
+    out = {"metric": METRIC}
+    legs = set(args.legs.split(",")) if not args.no_extras else set()
+    value = None
+    if not args.skip_headline:
+        print(f"bench: {args.workload} set-up", file=sys.stderr, flush=True)
+        head = bench_workload(torch, qlora, synth, args.workload, args.steps, args.warmup)
+        value = head["value"]
+        out.update({
+            "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": head["workload"] + " (NF4 + double quant base resident in HBM, LoRA fwd+bwd on "
+                                   "every linear)",
+                       "tokens": head["tokens"], "r": head["r"], "alpha": head["alpha"], "layers": head["layers"],
+                       "linears": head["linears"], "parallelism": "single GPU",
+                       "flop_per_step": head["flop_per_step"]},
+            "frac_of_bf16_peak": head["frac_of_bf16_peak"],
+            "roofline": head["roofline"],
+            "kernels": head["kernels"],
+            "quantize_all": head["quantize_all"],
+        })
+        print(f"bench: {args.workload} {value} TFLOP/s", file=sys.stderr, flush=True)
+    if "workloads" in legs:
         out["workloads"] = {}
         for key in ("layer33b", "mlp7b"):
             if key == args.workload:
@@ -535,18 +649,27 @@ def main():
             res = bench_workload(torch, qlora, synth, key, 10 if key == "layer33b" else 20, 3)
             res.pop("kernels")
             out["workloads"][key] = res
+    if "gemv" in legs:
         print("bench: gemv", file=sys.stderr, flush=True)
         out["gemv"] = bench_gemv(torch, qlora, synth)
+    if "gemv_grouped" in legs:
+        print("bench: gemv grouped", file=sys.stderr, flush=True)
+        out["gemv_grouped"] = bench_gemv_grouped(torch, qlora, synth)
+    if "quantize" in legs:
         print("bench: quantize", file=sys.stderr, flush=True)
         out["quantize"] = bench_quantize(torch, qlora)
+    if "peaks" in legs:
         print("bench: peaks", file=sys.stderr, flush=True)
         peaks = measure_peaks(torch)
-        if peaks is not None:
+        if peaks is not None and value is not None:
             peaks["headline_frac_of_measured_mfma"] = round(value / peaks["mfma_bf16_TFLOPs"], 4)
-            if head["roofline"]:
-                peaks["roofline_frac_of_measured_mfma"] = round(head["roofline"]["achieved"] /
+            if out.get("roofline"):
+                peaks["roofline_frac_of_measured_mfma"] = round(out["roofline"]["achieved"] /
                                                                peaks["mfma_bf16_TFLOPs"], 4)
-            peaks["gemv_frac_of_measured_copy"] = round(out["gemv"]["value"] / peaks["copy_GBs"], 4)
+        if peaks is not None:
+            for leg in ("gemv", "gemv_grouped"):
+                if leg in out:
+                    peaks[f"{leg}_frac_of_measured_copy"] = round(out[leg]["value"] / peaks["copy_GBs"], 4)
         out["peaks"] = peaks
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)

@@ -84,7 +84,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // contraction slices of the rest), so the slices of a tile share an L2.
   const TileItem it = decode_item(p.plan, blockIdx.x);
   if (it.tile < 0) return;  // uniform per workgroup, before any barrier
-  const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
+  // Tiles are numbered problem-major over the batch.
+  const int tile_g = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
+  const int bat = __builtin_amdgcn_readfirstlane(tile_g / p.tiles_per);
+  const int tile = tile_g - bat * p.tiles_per;
+  const DxGemmProblem& P = p.prob[bat];
   // Workgroup-uniform values kept in scalar registers (the buffer views
   // built from them must be uniform).
   const int tk = __builtin_amdgcn_readfirstlane(tile % p.tiles_k);
@@ -114,10 +118,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // Buffer views: loads past the end return zero.  Codes of rows n >= N
   // read zero and their scales are zero, so those W' rows vanish; k past K
   // has zero scales too.  dY rows are viewed from this tile's first row.
-  const rsrc_t rc = make_rsrc(p.codes, N * K2);
-  const rsrc_t rq = make_rsrc(p.q8, N * bpr);
-  const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
-  const rsrc_t rd = make_rsrc(p.dY + t0 * N, (T - t0) * N * 2);
+  const rsrc_t rc = make_rsrc(P.codes, N * K2);
+  const rsrc_t rq = make_rsrc(P.q8, N * bpr);
+  const rsrc_t rs = make_rsrc(P.s2, ((N * bpr + 255) / 256) * 4);
+  const rsrc_t rd = make_rsrc(P.dY + t0 * N, (T - t0) * N * 2);
   const uint32_t coff = (uint32_t)((8 * rg) * K2 + kcol / 2);
   auto load_code = [&](int j, int i) -> uint32_t { return buf_load4(rc, coff + (uint32_t)(j * 64 * K2 + i * K2)); };
   // Codes of later steps go through LDS: wave w copies rows 16w .. 16w+15
@@ -330,9 +334,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
   // zero through an out-of-range offset.
   const int r = p.r;
   if (sidx == 0) {
-    const rsrc_t ra = make_rsrc(p.A + k0 * r, (K - k0) * r * 2);
-    const rsrc_t rgh = make_rsrc(p.Gh + t0 * p.RP, (T - t0) * p.RP * 2);
-    const rsrc_t rgl = make_rsrc(p.Gl + t0 * p.RP, (T - t0) * p.RP * 2);
+    const rsrc_t ra = make_rsrc(P.A + k0 * r, (K - k0) * r * 2);
+    const rsrc_t rgh = make_rsrc(P.Gh + t0 * p.RP, (T - t0) * p.RP * 2);
+    const rsrc_t rgl = make_rsrc(P.Gl + t0 * p.RP, (T - t0) * p.RP * 2);
     const int drow = lane >> 3, dphys = lane & 7;
     for (int jb = 0; jb < p.RP; jb += 64) {
       __syncthreads();  // every wave is done with the buffers
@@ -399,19 +403,27 @@ __global__ __launch_bounds__(256, 1) void gemm_dx_kernel(DxGemmParams p, Codeboo
     const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;
     const int64_t t = t0 + row, k = k0 + 8 * c;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * 512 + ((c ^ (row & 31)) << 4));
-    if (t < T && k < K) *reinterpret_cast<u32x4*>(p.dX + t * K + k) = v;  // K % 64 == 0: chunks whole
+    if (t < T && k < K) *reinterpret_cast<u32x4*>(P.dX + t * K + k) = v;  // K % 64 == 0: chunks whole
   }
 }
 
-SplitPlan dx_plan(int64_t T, int64_t K, int64_t N) {
-  return make_split_plan(((K + kTileK - 1) / kTileK) * ((T + kTileT - 1) / kTileT), (N + 63) / 64);
+SplitPlan dx_plan(int64_t T, int64_t K, int64_t N, int batch) {
+  return make_split_plan((int64_t)batch * ((K + kTileK - 1) / kTileK) * ((T + kTileT - 1) / kTileT), (N + 63) / 64);
 }
 
 hipError_t launch_gemm_dx(const DxGemmParams& p0, const Codebook& cb, hipStream_t s) {
   DxGemmParams p = p0;
+  p.batch = 1;
+  p.prob[0] = DxGemmProblem{p.dY, p.codes, p.q8, p.s2, p.A, p.Gh, p.Gl, p.dX};
+  return launch_gemm_dx_batched(p, cb, s);
+}
+
+hipError_t launch_gemm_dx_batched(const DxGemmParams& p0, const Codebook& cb, hipStream_t s) {
+  DxGemmParams p = p0;
   p.tiles_k = (int)((p.K + kTileK - 1) / kTileK);
   p.tiles_t = (int)((p.T + kTileT - 1) / kTileT);
-  p.plan = dx_plan(p.T, p.K, p.N);
+  p.tiles_per = p.tiles_k * p.tiles_t;
+  p.plan = dx_plan(p.T, p.K, p.N, p.batch);
   {
     KernelTimer kt_("gemm_dx_kernel", s);
     hipLaunchKernelGGL(gemm_dx_kernel, dim3(8 * p.plan.items), dim3(256), 0, s, p, cb);

@@ -71,7 +71,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // Items are (tile, contraction slice) pairs, slices of a tile adjacent.
   const TileItem it = decode_item(p.plan, blockIdx.x);
   if (it.tile < 0) return;  // uniform per workgroup, before any barrier
-  const int tile = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
+  // Tiles are numbered problem-major over the batch.
+  const int tile_g = __builtin_amdgcn_readfirstlane(it.tile), sidx = __builtin_amdgcn_readfirstlane(it.sidx);
+  const int bat = __builtin_amdgcn_readfirstlane(tile_g / p.tiles_per);
+  const int tile = tile_g - bat * p.tiles_per;
+  const FwdGemmProblem& P = p.prob[bat];
   const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
 
   codebook_to_lds(lut16, cb, tid);
@@ -85,10 +89,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   auto clampk = [&](int k) { return k < nk ? k : nk - 1; };  // past the end: redundant, in bounds
 
   // Buffer views of this tile's rows: reads past the last row return zero.
-  const rsrc_t rx = make_rsrc(p.X + m0 * K, (T - m0) * K * 2);
-  const rsrc_t rc = make_rsrc(p.codes + n0 * K2, (N - n0) * K2);
-  const rsrc_t rq = make_rsrc(p.q8 + n0 * bpr, (N - n0) * bpr);
-  const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
+  const rsrc_t rx = make_rsrc(P.X + m0 * K, (T - m0) * K * 2);
+  const rsrc_t rc = make_rsrc(P.codes + n0 * K2, (N - n0) * K2);
+  const rsrc_t rq = make_rsrc(P.q8 + n0 * bpr, (N - n0) * bpr);
+  const rsrc_t rs = make_rsrc(P.s2, ((N * bpr + 255) / 256) * 4);
 
   int nl[2];
   bool nval[2];
@@ -282,8 +286,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   // into the swizzled X-stage layout.
   if (sidx == 0) {
     const int r = p.r;
-    const rsrc_t rh = make_rsrc(p.XAh + m0 * p.RP, (T - m0) * p.RP * 2);
-    const rsrc_t rl = make_rsrc(p.XAl + m0 * p.RP, (T - m0) * p.RP * 2);
+    const rsrc_t rh = make_rsrc(P.XAh + m0 * p.RP, (T - m0) * p.RP * 2);
+    const rsrc_t rl = make_rsrc(P.XAl + m0 * p.RP, (T - m0) * p.RP * 2);
     const int bjg = tid & 7, bng = tid >> 3;  // lane's 8 j and 8 n of the B tile
     const int64_t bn = n0 + 8 * bng;
     const int drow = lane >> 3, dphys = lane & 7;
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = jb + 8 * bjg + i;
-        brow[i] = (j < r && bn < N) ? *reinterpret_cast<const u32x4*>(p.B + (int64_t)j * N + bn)
+        brow[i] = (j < r && bn < N) ? *reinterpret_cast<const u32x4*>(P.B + (int64_t)j * N + bn)
                                     : u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();  // every wave is done with the stages
@@ -368,19 +372,27 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
     const int idx = 256 * i + tid, row = idx >> 5, c = idx & 31;  // row 0..255 = 64 * (i / 8) + ..
     const int64_t m = m0 + row, n = n0 + 8 * c;
     const u32x4 v = *reinterpret_cast<const u32x4*>(xring[i >> 3] + (row & 63) * 512 + ((c ^ (row & 31)) << 4));
-    if (m < T && n < N) *reinterpret_cast<u32x4*>(p.Y + m * N + n) = v;  // N % 8 == 0: chunks whole
+    if (m < T && n < N) *reinterpret_cast<u32x4*>(P.Y + m * N + n) = v;  // N % 8 == 0: chunks whole
   }
 }
 
-SplitPlan fwd_plan(int64_t T, int64_t K, int64_t N) {
-  return make_split_plan(((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM), K / 64);
+SplitPlan fwd_plan(int64_t T, int64_t K, int64_t N, int batch) {
+  return make_split_plan((int64_t)batch * ((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM), K / 64);
 }
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p0, const Codebook& cb, hipStream_t s) {
   FwdGemmParams p = p0;
+  p.batch = 1;
+  p.prob[0] = FwdGemmProblem{p.X, p.codes, p.q8, p.s2, p.B, p.XAh, p.XAl, p.Y};
+  return launch_gemm_fwd_batched(p, cb, s);
+}
+
+hipError_t launch_gemm_fwd_batched(const FwdGemmParams& p0, const Codebook& cb, hipStream_t s) {
+  FwdGemmParams p = p0;
   p.tiles_n = (int)((p.N + kTileN - 1) / kTileN);
   p.tiles_m = (int)((p.T + kTileM - 1) / kTileM);
-  p.plan = fwd_plan(p.T, p.K, p.N);
+  p.tiles_per = p.tiles_n * p.tiles_m;
+  p.plan = fwd_plan(p.T, p.K, p.N, p.batch);
   {
     KernelTimer kt_("gemm_fwd_kernel", s);
     hipLaunchKernelGGL(gemm_fwd_kernel, dim3(8 * p.plan.items), dim3(256), 0, s, p, cb);

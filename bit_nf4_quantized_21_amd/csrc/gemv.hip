@@ -21,7 +21,13 @@
 // contraction on MFMA and stores the fp32 partial).  The GEMV requests the
 // partials right behind its first weight loads and adds them in slice order
 // in its epilogue, so XA is the same in every workgroup and does not depend
-// on timing; workgroup 0 also returns it.
+// on timing; the linear's first workgroup also returns it.
+//
+// Both kernels serve a group of up to kGemvGroupMax linears in one launch
+// (the grouped small-token path: q/k/v, gate/up, or every linear of a
+// layer at once): each linear owns a contiguous range of workgroups, so the
+// launch and ramp are paid once for the whole group and the weight streams
+// of all its linears overlap.  A single linear is a group of one.
 #include "common.hpp"
 #include "timing.hpp"
 #include "gemm.hpp"
@@ -32,12 +38,12 @@ namespace {
 constexpr int kRowsPerWG = 16;
 constexpr int kWaves = 8;  // of the GEMV; the XA partial kernel has 8 too
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 2;    // chunks in flight per wave
 constexpr int kMaxR = 128;
 constexpr int kAWinBytes = 65536;  // A window of an XA workgroup in LDS
 constexpr int kXWin = 512;         // widest k window (RP = 64)
 constexpr int kXPitch = kXWin + 8; // bf16 per staged X row
-constexpr int kPartRegs = 32;      // XA partial values one GEMV thread holds
+constexpr int kMaxParts = 32;           // XA partial slices per linear
+constexpr int kPartLdsBytes = 36864;    // LDS area of the XA partials / the wave sums
 constexpr int kXaPitch = kMaxR + 4;  // floats per row of XA / B^T in LDS (16-byte rows)
 }  // namespace
 
@@ -48,15 +54,25 @@ constexpr int kXaPitch = kMaxR + 4;  // floats per row of XA / B^T in LDS (16-by
 // (8 / (RP/16))-th 32-k step of each window, starting at w / (RP/16).  A
 // window's rows of A are contiguous, so they are staged with plain 16-byte
 // loads and read back column-wise from LDS.
-__global__ __launch_bounds__(512) void xa_partial_kernel(const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ A, float* __restrict__ P,
-                                                         int T, int64_t K, int r, int RP, int ks) {
+__global__ __launch_bounds__(512) void xa_partial_kernel(GemvGroup G) {
+  // The linear of this workgroup (uniform: a scalar search over the group).
+  int li = 0;
+#pragma unroll
+  for (int j = 1; j < kGemvGroupMax; ++j)
+    if (j < G.count && (int)blockIdx.x >= G.L[j].part_begin) li = j;
+  const GemvLinear& Lin = G.L[li];
+  const uint16_t* __restrict__ X = Lin.X;
+  const uint16_t* __restrict__ A = Lin.A;
+  float* __restrict__ P = Lin.P;
+  const int T = G.T, r = G.r, RP = G.RP, ks = Lin.ks;
+  const int64_t K = Lin.K;
+  const int pb = (int)blockIdx.x - Lin.part_begin;  // slice of this linear
   __shared__ __align__(16) uint16_t as_[kAWinBytes / 2];
   __shared__ __align__(16) uint16_t xs_[16 * kXPitch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   const int kw = kAWinBytes / 2 / RP;  // 512 (RP = 64) or 256 (RP = 128)
-  const int64_t kb0 = (int64_t)blockIdx.x * ks;
+  const int64_t kb0 = (int64_t)pb * ks;
   const int64_t kb1 = kb0 + ks < K ? kb0 + ks : K;
   const rsrc_t ra = make_rsrc(A, K * r * 2);
   const rsrc_t rx = make_rsrc(X, (int64_t)T * K * 2);
@@ -112,55 +128,72 @@ __global__ __launch_bounds__(512) void xa_partial_kernel(const uint16_t* __restr
     const int t = v / RP, jj = v % RP;
     float sum = xt[jj * 17 + t];
     for (int h = 1; h < wpt; ++h) sum += xt[(h * RP + jj) * 17 + t];
-    P[(int64_t)blockIdx.x * nvals + v] = sum;
+    P[(int64_t)pb * nvals + v] = sum;
   }
 }
 
+// Registers of one 128-k chunk of a wave: RG row groups of 16 rows share
+// one set of X operands.
+template <int RG>
 struct ChunkRegs {
-  u32x4 c;      // 32 codes of this lane
-  uint32_t q;   // q8 of the lane's block
-  float s2;     // s2 of that block's group
-  u32x4 x[4];   // X[t][k0 + 8s .. +8], s = 0..3
+  u32x4 c[RG];     // 32 codes of this lane's row in each row group
+  uint32_t q[RG];  // q8 of the lane's block in each row group
+  float s2[RG];    // s2 of those blocks' groups
+  u32x4 x[4];      // X[t][k0 + 8s .. +8], s = 0..3
 };
 
-// NQ: XA values per thread (T * RP <= kThreads NQ); the thread holds all
-// kPartRegs / NQ slices of each.
-template <int NQ>
-__global__ __launch_bounds__(kThreads) void gemv_fwd_kernel(FwdGemmParams p, Codebook cb) {
-  constexpr int NP = kPartRegs / NQ;
-  __shared__ __align__(4096) unsigned char tbl[2048];  // codebook pair table at LDS address 0
-  __shared__ float red[kWaves][16][17];
-  __shared__ __align__(16) float xa_s[16][kXaPitch];  // XA[t][j]
-  __shared__ __align__(16) float bt_s[16][kXaPitch];  // B[j][n0 + nn] at [nn][j]
+// RG: row groups of 16 rows per workgroup (and per wave chunk).  More row
+// groups put more weight bytes in flight per wave (4 KiB per chunk at
+// RG = 4) and share each X load among more rows; the launcher picks RG so
+// the grid still fills the GPU.
+template <int RG>
+__global__ __launch_bounds__(kThreads) void gemv_fwd_kernel(GemvGroup G, Codebook cb) {
+  constexpr int ROWS = 16 * RG;
+  static_assert(kWaves * ROWS * 17 * 4 <= kPartLdsBytes, "wave sums fit the partial area");
+  int li = 0;
+#pragma unroll
+  for (int j = 1; j < kGemvGroupMax; ++j)
+    if (j < G.count && (int)blockIdx.x >= G.L[j].wg_begin) li = j;
+  const GemvLinear& p = G.L[li];
+  const int bid = (int)blockIdx.x - p.wg_begin;  // workgroup of this linear
+  __shared__ __align__(4096) unsigned char tbl[2048];    // codebook pair table at LDS address 0
+  // XA partials [nparts][T][RP] (copied in at the start); after they are
+  // summed, the waves' partial outputs [kWaves][ROWS][17].
+  __shared__ __align__(16) float ps[kPartLdsBytes / 4];
+  __shared__ __align__(16) float xa_s[16][kXaPitch];       // XA[t][j]
+  __shared__ __align__(16) uint16_t b_s[kMaxR * ROWS];     // B[j][n0 + nn] at j * ROWS + nn
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t T = p.T, K = p.K, N = p.N;
-  const int r = p.r, RP = p.RP;
-  const int64_t n0 = (int64_t)blockIdx.x * kRowsPerWG;
-  const int64_t n = n0 + l16;
+  const int64_t T = G.T, K = p.K, N = p.N;
+  const int r = G.r, RP = G.RP;
+  const int64_t n0 = (int64_t)bid * ROWS;
   const int64_t K2 = K / 2, bpr = K / 64;
 
   const int64_t nchunk = (K + 127) / 128;
-  // Unconditional buffer loads (reads past a view's end return zero): rows
-  // n >= N read zero codes and scales; a 32-k group past K reads some other
-  // row's codes but a zero X (its offset is pushed out of range), so it adds
-  // nothing.
   const rsrc_t rc = make_rsrc(p.codes, N * K2);
   const rsrc_t rq = make_rsrc(p.q8, N * bpr);
   const rsrc_t rs = make_rsrc(p.s2, ((N * bpr + 255) / 256) * 4);
   const rsrc_t rx = make_rsrc(p.X, T * K * 2);
-  // Chunks past the last one are not requested (a branch uniform over the
-  // wave): even a load that returns zero would take a slot in the memory
-  // pipeline and hold its registers until it drains.
-  auto load = [&](int64_t c, ChunkRegs& R) {
-    if (c >= nchunk) return;
-    const int64_t k0 = c * 128 + 32 * g;
-    const bool kv = k0 < K;  // K % 64 == 0: a 32-k group is whole or absent
-    R.c = buf_load16(rc, (uint32_t)(n * K2 + k0 / 2));
-    const int64_t b = n * bpr + k0 / 64;
-    R.q = buf_load1(rq, (uint32_t)b);
-    R.s2 = __uint_as_float(buf_load4(rs, (uint32_t)((b >> 8) * 4)));
+  // This wave's chunks are c = wave + 8 m, m < nmine.
+  const int nmine = nchunk > wave ? (int)((nchunk - wave + kWaves - 1) / kWaves) : 0;
+  // Unconditional buffer loads (reads past a view's end return zero): rows
+  // n >= N read zero codes and scales; a 32-k group past K, and every load
+  // of a chunk m >= nmine, has its offset pushed out of range, so it reads
+  // zero without memory traffic.  With no branch around the loads, the
+  // compiler counts the loads in flight exactly and waits only for the
+  // chunk it is about to use.
+  auto load = [&](int m, ChunkRegs<RG>& R) {
+    const int64_t k0 = (int64_t)(wave + kWaves * m) * 128 + 32 * g;
+    const bool kv = m < nmine && k0 < K;  // K % 64 == 0: a 32-k group is whole or absent
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const int64_t n = n0 + 16 * rg + l16;
+      R.c[rg] = buf_load16(rc, off_if(kv, (uint32_t)(n * K2 + k0 / 2)));
+      const int64_t b = n * bpr + k0 / 64;
+      R.q[rg] = buf_load1(rq, off_if(kv, (uint32_t)b));
+      R.s2[rg] = __uint_as_float(buf_load4(rs, off_if(kv, (uint32_t)((b >> 8) * 4))));
+    }
     // Lanes of padding tokens (l16 >= T) read past the X view: zero, and no
     // memory traffic (an exec-masked load would cost more than this).
     const uint32_t xo = off_if(kv, (uint32_t)(((int64_t)l16 * K + k0) * 2));
@@ -168,111 +201,105 @@ __global__ __launch_bounds__(kThreads) void gemv_fwd_kernel(FwdGemmParams p, Cod
     for (int s = 0; s < 4; ++s) R.x[s] = buf_load16(rx, xo + 16 * s);
   };
 
-  // The codebook pair table first (a barrier with no load outstanding costs
-  // little), then the weight stream: four chunks of every wave in flight.
-  pair_table_from_arg(tbl, cb, tid);
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  ChunkRegs R[kRing] = {};
-  const int64_t c0 = wave;
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) load(c0 + i * kWaves, R[i]);
-
-  // Then the XA partials this thread adds: part[q][b] is slice b of value
-  // v = tid + kThreads q (slices past nparts read zero), and the workgroup's
-  // r x 16 slice of B (value v = tid + kThreads q is B[v/16][n0 + v%16]).
+  // First the XA partials and the workgroup's B slice, copied straight into
+  // LDS by buffer-to-LDS loads (no registers held; bytes past either view
+  // read zero), then the codebook pair table, then the weight stream.
   const int nvals = (int)T * RP, nparts = p.nparts;
-  const rsrc_t rp = make_rsrc(p.P, (int64_t)nparts * nvals * 4);
-  float part[NQ][NP];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int b = 0; b < NP; ++b) part[q][b] = 0.0f;
-  if (wave * 64 < nvals) {  // waves whose first value is past the end hold none
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int v = tid + kThreads * q;
-#pragma unroll
-      for (int b = 0; b < NP; ++b)
-        part[q][b] = __uint_as_float(buf_load4(rp, off_if(v < nvals && b < nparts, (uint32_t)((b * nvals + v) * 4))));
+  {
+    const rsrc_t rp = make_rsrc(p.P, (int64_t)nparts * nvals * 4);
+    const int units = (nparts * nvals * 4 + 15) / 16;
+    for (int u0 = wave * 64; u0 < units; u0 += kThreads)
+      buf_load16_to_lds(rp, reinterpret_cast<unsigned char*>(ps) + u0 * 16, (uint32_t)((u0 + lane) * 16));
+    // B row j, 16-byte unit cu of the workgroup's ROWS columns; rows j >= r
+    // read zero.
+    const rsrc_t rb = make_rsrc(p.B, (int64_t)r * N * 2);
+    constexpr int kUnitsPerRow = ROWS / 8;
+    for (int u0 = wave * 64; u0 < r * kUnitsPerRow; u0 += kThreads) {
+      const int u = u0 + lane, j = u / kUnitsPerRow, cu = u % kUnitsPerRow;
+      buf_load16_to_lds(rb, reinterpret_cast<unsigned char*>(b_s) + u0 * 16,
+                        off_if(u < r * kUnitsPerRow, (uint32_t)(((int64_t)j * N + n0 + 8 * cu) * 2)));
     }
   }
-  const int nbv = r * kRowsPerWG;
-  const rsrc_t rb = make_rsrc(p.B, (int64_t)r * N * 2);
-  constexpr int kBq = kMaxR * kRowsPerWG / kThreads;
-  uint32_t bv[kBq];
+  pair_table_from_arg(tbl, cb, tid);
+  lds_barrier();  // the pair table (the copies above stay in flight)
+  f32x4 acc[RG];
 #pragma unroll
-  for (int q = 0; q < kBq; ++q) {
-    const int v = tid + kThreads * q;
-    const int64_t nn = n0 + v % kRowsPerWG;
-    bv[q] = buf_load2(rb, off_if(v < nbv && nn < N, (uint32_t)(((int64_t)(v / kRowsPerWG) * N + nn) * 2)));
-  }
-  for (int64_t cb0 = c0; cb0 < nchunk; cb0 += kRing * kWaves) {
+  for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  ChunkRegs<RG> R[2];
+  load(0, R[0]);
+  load(1, R[1]);
+  auto compute = [&](const ChunkRegs<RG>& C) {
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int64_t c = cb0 + i * kWaves;
-      if (c >= nchunk) break;
-      const float sc = dq_scale(R[i].q, R[i].s2);
+    for (int rg = 0; rg < RG; ++rg) {
+      const float sc = dq_scale(C.q[rg], C.s2[rg]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float f[8];
-        lut8_pairs(tbl, R[i].c[s], f);
-        acc = mfma16(as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
-                               pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)),
-                     as_bf16x8(R[i].x[s]), acc);
-      }
-      load(c + kRing * kWaves, R[i]);
-    }
-  }
-  // D[n][t]: lane holds column t = l16 and rows n = 4g + i.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * g + i][l16] = acc[i];
-#pragma unroll
-  for (int q = 0; q < kBq; ++q) {
-    const int v = tid + kThreads * q;
-    if (v < nbv) bt_s[v % kRowsPerWG][v / kRowsPerWG] = bf16_to_f32((uint16_t)bv[q]);
-  }
-  // XA = the partials added in slice order; workgroup 0 also returns it.
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int v = tid + kThreads * q;
-    float x = part[q][0];
-#pragma unroll
-    for (int b = 1; b < NP; ++b) x += part[q][b];
-    if (v < nvals) {
-      const int t = v / RP, jj = v % RP;
-      if (jj < r) {
-        xa_s[t][jj] = x;
-        if (blockIdx.x == 0) p.XA[t * r + jj] = x;
+        lut8_pairs(tbl, C.c[rg][s], f);
+        acc[rg] = mfma16(as_bf16x8(pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                                   pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)),
+                         as_bf16x8(C.x[s]), acc[rg]);
       }
     }
+  };
+  // Pairs of chunks loop, the odd last chunk runs once after the loop, so
+  // the back-edge is reached from one path and the wait counts stay exact:
+  // each chunk waits only for its own loads, the next chunk's stay in
+  // flight.
+  int m = 0;
+  for (; m + 2 <= nmine; m += 2) {
+    compute(R[0]);
+    load(m + 2, R[0]);
+    compute(R[1]);
+    load(m + 3, R[1]);
   }
+  if (m < nmine) compute(R[0]);
+
+  // XA = the partials added in slice order; the linear's first workgroup
+  // also returns it.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies into LDS
+  __syncthreads();
+  for (int v = tid; v < nvals; v += kThreads) {
+    float x = ps[v];
+    for (int b = 1; b < nparts; ++b) x += ps[b * nvals + v];
+    const int t = v / RP, jj = v % RP;
+    if (jj < r) {
+      xa_s[t][jj] = x;
+      if (bid == 0) p.XA[t * r + jj] = x;
+    }
+  }
+  __syncthreads();  // the partials are consumed: their area takes the wave sums
+  // D[n][t]: lane holds column t = l16 and rows 16 rg + 4g + i.
+  float* const red = ps;
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * ROWS + 16 * rg + 4 * g + i) * 17 + l16] = acc[rg][i];
   __syncthreads();
 
-  if (tid < 256) {
-    const int t = tid >> 4, nn = tid & 15;
-    if (t < T && n0 + nn < N) {
+  for (int o = tid; o < (int)T * ROWS; o += kThreads) {
+    const int t = o / ROWS, nn = o % ROWS;
+    if (n0 + nn < N) {
       float y = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) y += red[w][nn][t];
+      for (int w = 0; w < kWaves; ++w) y += red[(w * ROWS + nn) * 17 + t];
       // s XA[t] . B[:, n]: r % 8 == 0; two interleaved sums, added at the end.
       float lo0 = 0.0f, lo1 = 0.0f;
       for (int j = 0; j < r; j += 8) {
         const float4 a0 = *reinterpret_cast<const float4*>(&xa_s[t][j]);
         const float4 a1 = *reinterpret_cast<const float4*>(&xa_s[t][j + 4]);
-        const float4 b0 = *reinterpret_cast<const float4*>(&bt_s[nn][j]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&bt_s[nn][j + 4]);
-        lo0 += a0.x * b0.x;
-        lo1 += a0.y * b0.y;
-        lo0 += a0.z * b0.z;
-        lo1 += a0.w * b0.w;
-        lo0 += a1.x * b1.x;
-        lo1 += a1.y * b1.y;
-        lo0 += a1.z * b1.z;
-        lo1 += a1.w * b1.w;
+        const uint16_t* bj = b_s + j * ROWS + nn;
+        lo0 += a0.x * bf16_to_f32(bj[0 * ROWS]);
+        lo1 += a0.y * bf16_to_f32(bj[1 * ROWS]);
+        lo0 += a0.z * bf16_to_f32(bj[2 * ROWS]);
+        lo1 += a0.w * bf16_to_f32(bj[3 * ROWS]);
+        lo0 += a1.x * bf16_to_f32(bj[4 * ROWS]);
+        lo1 += a1.y * bf16_to_f32(bj[5 * ROWS]);
+        lo0 += a1.z * bf16_to_f32(bj[6 * ROWS]);
+        lo1 += a1.w * bf16_to_f32(bj[7 * ROWS]);
       }
       const float lo = lo0 + lo1;
-      y += p.s * lo;
+      y += G.s * lo;
       const uint32_t v = pack_bf16x2(y, 0.0f);
       p.Y[(int64_t)t * N + n0 + nn] = (uint16_t)(v & 0xFFFF);
     }
@@ -284,8 +311,9 @@ GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r) {
   g.grid = (int)((N + kRowsPerWG - 1) / kRowsPerWG);
   const int64_t RP = (r + 63) / 64 * 64;
   int64_t np = (K + 127) / 128;  // slices of at least 128 k
-  const int64_t nq = (T * RP + kThreads - 1) / kThreads;
-  const int64_t cap = kPartRegs / (nq <= 1 ? 1 : nq <= 2 ? 2 : 4);
+  // the partials of all slices must fit the GEMV's LDS area
+  int64_t cap = (int64_t)(kPartLdsBytes / 4) / (T * RP);
+  if (cap > kMaxParts) cap = kMaxParts;
   if (np > cap) np = cap;
   if (np < 1) np = 1;
   const int64_t ks = ((K + np - 1) / np + 31) / 32 * 32;
@@ -294,25 +322,61 @@ GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r) {
   return g;
 }
 
-hipError_t launch_gemv_fwd(const FwdGemmParams& p0, const Codebook& cb, hipStream_t s) {
-  FwdGemmParams p = p0;
-  const GemvPlan g = gemv_plan(p.N, p.K, p.T, p.r);
-  p.nparts = g.nparts;
+hipError_t launch_gemv_group(GemvGroup g, const Codebook& cb, hipStream_t s) {
+  // Row groups per workgroup: the most (4, 2, 1) that still gives at least
+  // four workgroups per compute unit over the whole group.
+  int RG = 4;
+  for (; RG > 1; RG /= 2) {
+    int64_t wgs = 0;
+    for (int i = 0; i < g.count; ++i) wgs += (g.L[i].N + 16 * RG - 1) / (16 * RG);
+    if (wgs >= 1024) break;
+  }
+  int wg = 0, parts = 0;
+  for (int i = 0; i < g.count; ++i) {
+    GemvLinear& L = g.L[i];
+    const GemvPlan pl = gemv_plan(L.N, L.K, g.T, g.r);
+    L.nparts = pl.nparts;
+    L.ks = pl.ks;
+    L.wg_begin = wg;
+    L.part_begin = parts;
+    wg += (int)((L.N + 16 * RG - 1) / (16 * RG));
+    parts += pl.nparts;
+  }
   {
     KernelTimer kt_("xa_partial_kernel", s);
-    hipLaunchKernelGGL(xa_partial_kernel, dim3(g.nparts), dim3(512), 0, s, p.X, p.A, p.P, (int)p.T, p.K, p.r, p.RP,
-                       g.ks);
+    hipLaunchKernelGGL(xa_partial_kernel, dim3(parts), dim3(512), 0, s, g);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("gemv_fwd_kernel", s);
-    const int64_t nvals = p.T * p.RP;
-    if (nvals <= kThreads) hipLaunchKernelGGL(gemv_fwd_kernel<1>, dim3(g.grid), dim3(kThreads), 0, s, p, cb);
-    else if (nvals <= 2 * kThreads) hipLaunchKernelGGL(gemv_fwd_kernel<2>, dim3(g.grid), dim3(kThreads), 0, s, p, cb);
-    else hipLaunchKernelGGL(gemv_fwd_kernel<4>, dim3(g.grid), dim3(kThreads), 0, s, p, cb);
+    if (RG == 4) hipLaunchKernelGGL(gemv_fwd_kernel<4>, dim3(wg), dim3(kThreads), 0, s, g, cb);
+    else if (RG == 2) hipLaunchKernelGGL(gemv_fwd_kernel<2>, dim3(wg), dim3(kThreads), 0, s, g, cb);
+    else hipLaunchKernelGGL(gemv_fwd_kernel<1>, dim3(wg), dim3(kThreads), 0, s, g, cb);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s) {
+  GemvGroup g{};
+  g.count = 1;
+  g.T = (int)p.T;
+  g.r = p.r;
+  g.RP = p.RP;
+  g.s = p.s;
+  GemvLinear& L = g.L[0];
+  L.X = p.X;
+  L.codes = p.codes;
+  L.q8 = p.q8;
+  L.s2 = p.s2;
+  L.A = p.A;
+  L.B = p.B;
+  L.Y = p.Y;
+  L.XA = p.XA;
+  L.P = p.P;
+  L.K = p.K;
+  L.N = p.N;
+  return launch_gemv_group(g, cb, s);
 }
 
 }  // namespace qlora

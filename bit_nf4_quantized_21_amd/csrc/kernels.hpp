@@ -42,6 +42,41 @@ size_t bwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r);
 
 hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint16_t* X, uint16_t* Y, float* XA,
                              void* ws, hipStream_t s);
+// One linear of a grouped forward (all share T, r and alpha).
+struct GroupedLinear {
+  const uint16_t* X;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* Y;
+  float* XA;
+  int64_t K, N;
+};
+size_t fwd_grouped_workspace_bytes(int count, const GroupedLinear* L, int64_t T, int32_t r);
+
+// One linear of a grouped backward (all share T, r and alpha).
+struct GroupedLinearBwd {
+  const uint16_t* dY;
+  const uint16_t* X;
+  const float* XA;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* dX;
+  uint16_t* dA;
+  uint16_t* dB;
+  int64_t K, N;
+};
+size_t bwd_grouped_workspace_bytes(int count, const GroupedLinearBwd* L, int64_t T, int32_t r);
+hipError_t launch_linear_bwd_grouped(int count, const GroupedLinearBwd* L, int64_t T, int32_t r, float s,
+                                     const Codebook& cb, void* ws, hipStream_t st);
+hipError_t launch_linear_fwd_grouped(int count, const GroupedLinear* L, int64_t T, int32_t r, float s,
+                                     const Codebook& cb, void* ws, hipStream_t st);
+
 hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint16_t* dY, const uint16_t* X,
                              const float* XA, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, hipStream_t s);
 

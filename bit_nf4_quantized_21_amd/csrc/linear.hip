@@ -170,6 +170,263 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
   return a.T <= kGemvMaxT ? launch_gemv_fwd(p, cb, s) : launch_gemm_fwd(p, cb, s);
 }
 
+// ---------------------------------------------------------------------------
+// Batches of same-shape linears on the GEMM path (T > 16): each linear's
+// rank-r products run as usual, then ONE GEMM launch serves all their tiles
+// (problem-major tile order, one split plan), so small token counts fill
+// the GPU with whole-contraction tiles instead of contraction slices.
+// ---------------------------------------------------------------------------
+namespace {
+struct FwdBatchLayout {
+  size_t p, xah, slots, counters, total;
+  SplitPlan g;
+};
+FwdBatchLayout fwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
+  FwdBatchLayout l{};
+  l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
+  l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
+  l.g = fwd_plan(T, K, N, count);
+  l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
+  l.counters = align256((size_t)(l.g.nsplit() > 0 ? 2 * l.g.nsplit() : 1) * sizeof(int));
+  l.total = l.p + 2 * (size_t)count * l.xah + l.slots + l.counters;
+  return l;
+}
+struct BwdBatchLayout {
+  size_t pg, g, planes, ptok_b, ptok_a, slots, counters, total;
+  SplitPlan d;
+};
+BwdBatchLayout bwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
+  BwdBatchLayout l{};
+  const BwdLayout b = bwd_layout(T, K, N, r);
+  l.pg = b.pg;
+  l.g = b.g;
+  l.planes = b.planes;
+  l.ptok_b = b.ptok_b;
+  l.ptok_a = b.ptok_a;
+  l.d = dx_plan(T, K, N, count);
+  l.slots = l.d.S > 1 ? align256((size_t)l.d.nsplit() * l.d.S * kSplitSlotFloats * sizeof(float)) : 0;
+  l.counters = align256((size_t)(l.d.nsplit() > 0 ? 2 * l.d.nsplit() : 1) * sizeof(int));
+  l.total = l.pg + 2 * (size_t)count * l.g + 4 * l.planes + l.ptok_b + l.ptok_a + l.slots + l.counters;
+  return l;
+}
+}  // namespace
+
+size_t fwd_batch_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
+  if (T <= 0) return 0;
+  return fwd_batch_layout(T, K, N, r, count).total;
+}
+size_t bwd_batch_workspace_bytes(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
+  if (T <= 0) return 0;
+  return bwd_batch_layout(T, K, N, r, count).total;
+}
+
+hipError_t launch_linear_fwd_batch(int count, const GroupedLinear* L, int64_t T, int32_t r, float s,
+                                   const Codebook& cb, void* ws, hipStream_t st) {
+  const int64_t K = L[0].K, N = L[0].N;
+  const FwdBatchLayout l = fwd_batch_layout(T, K, N, r, count);
+  char* w = reinterpret_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(w);
+  char* wx = w + l.p;
+  char* w2 = wx + 2 * (size_t)count * l.xah;
+  int* counters = reinterpret_cast<int*>(w2 + l.slots);
+  FwdGemmParams p{};
+  hipError_t e = hipSuccess;
+  p.status = status_word(&e);
+  if (!p.status) return e;
+  for (int i = 0; i < count; ++i) {
+    uint16_t* XAh = reinterpret_cast<uint16_t*>(wx + (2 * (size_t)i) * l.xah);
+    uint16_t* XAl = reinterpret_cast<uint16_t*>(wx + (2 * (size_t)i + 1) * l.xah);
+    RowdotOut o{};
+    o.f32 = L[i].XA;
+    o.row_hi = XAh;
+    o.row_lo = XAl;
+    o.scale_row = s;
+    if (i == 0) {
+      o.zero = counters;  // the batched GEMM's split tickets
+      o.nzero = 2 * l.g.nsplit();
+    }
+    e = launch_rowdot(L[i].X, L[i].A, /*v_lr=*/true, P, o, T, K, r, row_chunk(T, K), st);
+    if (e != hipSuccess) return e;
+    p.prob[i] = FwdGemmProblem{L[i].X, L[i].codes, L[i].q8, L[i].s2, L[i].B, XAh, XAl, L[i].Y};
+  }
+  p.batch = count;
+  p.T = T;
+  p.K = K;
+  p.N = N;
+  p.r = r;
+  p.s = s;
+  p.RP = (int)rpad(r);
+  p.slots = reinterpret_cast<float*>(w2);
+  p.counters = counters;
+  return launch_gemm_fwd_batched(p, cb, st);
+}
+
+hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t T, int32_t r, float s,
+                                   const Codebook& cb, void* ws, hipStream_t st) {
+  const int64_t K = L[0].K, N = L[0].N;
+  if (T == 0) {
+    for (int i = 0; i < count; ++i) {
+      hipError_t e = launch_zero_u16(L[i].dA, K * r, st);
+      if (e != hipSuccess) return e;
+      e = launch_zero_u16(L[i].dB, (int64_t)r * N, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const BwdBatchLayout l = bwd_batch_layout(T, K, N, r, count);
+  char* w = reinterpret_cast<char*>(ws);
+  float* Pg = reinterpret_cast<float*>(w);
+  char* wg = w + l.pg;
+  char* w2 = wg + 2 * (size_t)count * l.g;
+  uint16_t* Gth = reinterpret_cast<uint16_t*>(w2);
+  uint16_t* Gtl = reinterpret_cast<uint16_t*>(w2 + l.planes);
+  uint16_t* XAth = reinterpret_cast<uint16_t*>(w2 + 2 * l.planes);
+  uint16_t* XAtl = reinterpret_cast<uint16_t*>(w2 + 3 * l.planes);
+  float* Ptok_b = reinterpret_cast<float*>(w2 + 4 * l.planes);
+  float* Ptok_a = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok_b);
+  char* w3 = w2 + 4 * l.planes + l.ptok_b + l.ptok_a;
+  int* counters = reinterpret_cast<int*>(w3 + l.slots);
+  const int64_t TP = round_up(T, 64);
+  DxGemmParams p{};
+  hipError_t e = hipSuccess;
+  p.status = status_word(&e);
+  if (!p.status) return e;
+  for (int i = 0; i < count; ++i) {
+    uint16_t* Gh = reinterpret_cast<uint16_t*>(wg + (2 * (size_t)i) * l.g);
+    uint16_t* Gl = reinterpret_cast<uint16_t*>(wg + (2 * (size_t)i + 1) * l.g);
+    RowdotOut o{};
+    o.row_hi = Gh;
+    o.row_lo = Gl;
+    o.scale_row = s;
+    o.t_hi = Gth;
+    o.t_lo = Gtl;
+    o.TP = TP;
+    o.side = L[i].XA;
+    o.side_hi = XAth;
+    o.side_lo = XAtl;
+    if (i == 0) {
+      o.zero = counters;  // the batched dX GEMM's split tickets
+      o.nzero = 2 * l.d.nsplit();
+    }
+    e = launch_rowdot(L[i].dY, L[i].B, /*v_lr=*/false, Pg, o, T, N, r, row_chunk(T, N), st);
+    if (e != hipSuccess) return e;
+    TokJob jb{}, ja{};
+    jb.M = L[i].dY;
+    jb.Sh = XAth;
+    jb.Sl = XAtl;
+    jb.P = Ptok_b;
+    jb.out = L[i].dB;
+    jb.C = N;
+    jb.TC = tok_chunk(T, N);
+    jb.scale = s;
+    jb.m_major = 0;
+    ja.M = L[i].X;
+    ja.Sh = Gth;
+    ja.Sl = Gtl;
+    ja.P = Ptok_a;
+    ja.out = L[i].dA;
+    ja.C = K;
+    ja.TC = tok_chunk(T, K);
+    ja.scale = s;
+    ja.m_major = 1;
+    e = launch_tokdot2(jb, ja, T, TP, r, st);
+    if (e != hipSuccess) return e;
+    p.prob[i] = DxGemmProblem{L[i].dY, L[i].codes, L[i].q8, L[i].s2, L[i].A, Gh, Gl, L[i].dX};
+  }
+  p.batch = count;
+  p.T = T;
+  p.K = K;
+  p.N = N;
+  p.r = r;
+  p.RP = (int)rpad(r);
+  p.slots = reinterpret_cast<float*>(w3);
+  p.counters = counters;
+  return launch_gemm_dx_batched(p, cb, st);
+}
+
+// Runs of consecutive linears with the same K and N, at most kGemmBatchMax
+// long, in order; calls f(first, count) for each.
+template <class L, class F>
+static hipError_t for_each_run(int count, const L* x, F f) {
+  for (int i = 0; i < count;) {
+    int n = 1;
+    while (i + n < count && n < kGemmBatchMax && x[i + n].K == x[i].K && x[i + n].N == x[i].N) ++n;
+    hipError_t e = f(i, n);
+    if (e != hipSuccess) return e;
+    i += n;
+  }
+  return hipSuccess;
+}
+
+size_t bwd_grouped_workspace_bytes(int count, const GroupedLinearBwd* L, int64_t T, int32_t r) {
+  size_t total = 0;
+  for_each_run(count, L, [&](int i, int n) {
+    const size_t b = bwd_batch_workspace_bytes(T, L[i].K, L[i].N, r, n);
+    total = total > b ? total : b;
+    return hipSuccess;
+  });
+  return total;
+}
+
+hipError_t launch_linear_bwd_grouped(int count, const GroupedLinearBwd* L, int64_t T, int32_t r, float s,
+                                     const Codebook& cb, void* ws, hipStream_t st) {
+  return for_each_run(count, L, [&](int i, int n) { return launch_linear_bwd_batch(n, L + i, T, r, s, cb, ws, st); });
+}
+
+// Grouped small-token forward: T <= 16 runs every chunk of up to
+// kGemvGroupMax linears as one XA-partial launch and one GEMV launch, each
+// linear's partials in its own workspace region; larger T runs each linear's
+// GEMM path in turn on the shared workspace.
+size_t fwd_grouped_workspace_bytes(int count, const GroupedLinear* L, int64_t T, int32_t r) {
+  if (T <= 0) return 0;
+  size_t total = 0;
+  if (T <= kGemvMaxT) {
+    for (int i = 0; i < count; ++i) total += fwd_layout(T, L[i].K, L[i].N, r).total;
+    return total;
+  }
+  for_each_run(count, L, [&](int i, int n) {
+    const size_t b = fwd_batch_workspace_bytes(T, L[i].K, L[i].N, r, n);
+    total = total > b ? total : b;
+    return hipSuccess;
+  });
+  return total;
+}
+
+hipError_t launch_linear_fwd_grouped(int count, const GroupedLinear* L, int64_t T, int32_t r, float s,
+                                     const Codebook& cb, void* ws, hipStream_t st) {
+  if (T == 0 || count == 0) return hipSuccess;
+  char* w = reinterpret_cast<char*>(ws);
+  if (T > kGemvMaxT)
+    return for_each_run(count, L, [&](int i, int n) { return launch_linear_fwd_batch(n, L + i, T, r, s, cb, ws, st); });
+  for (int i0 = 0; i0 < count; i0 += kGemvGroupMax) {
+    GemvGroup g{};
+    g.count = count - i0 < kGemvGroupMax ? count - i0 : kGemvGroupMax;
+    g.T = (int)T;
+    g.r = r;
+    g.RP = (int)rpad(r);
+    g.s = s;
+    for (int j = 0; j < g.count; ++j) {
+      const GroupedLinear& x = L[i0 + j];
+      GemvLinear& y = g.L[j];
+      y.X = x.X;
+      y.codes = x.codes;
+      y.q8 = x.q8;
+      y.s2 = x.s2;
+      y.A = x.A;
+      y.B = x.B;
+      y.Y = x.Y;
+      y.XA = x.XA;
+      y.K = x.K;
+      y.N = x.N;
+      y.P = reinterpret_cast<float*>(w);
+      w += fwd_layout(T, x.K, x.N, r).total;
+    }
+    hipError_t e = launch_gemv_group(g, cb, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint16_t* dY, const uint16_t* X,
                              const float* XA, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, hipStream_t s) {
   if (a.T == 0) {

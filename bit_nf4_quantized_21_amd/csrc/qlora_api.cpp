@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/qlora.h"
 #include "codebook.hpp"
@@ -255,6 +256,111 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N, const u
                      float* XA, void* workspace, size_t workspace_bytes, void* stream) {
   return qlora_linear_fwd_4bit(qlora::kQNF4, X, T, K, N, codes, q8, s2, A, B, r, alpha, Y, XA, workspace,
                                workspace_bytes, stream);
+}
+
+namespace {
+// Validates a group and converts it; returns a qlora_status.
+int check_group(int32_t count, const qlora_linear_desc* d, int64_t T, int32_t r,
+                std::vector<qlora::GroupedLinear>* out) {
+  if (count < 0 || count > 4096) return QLORA_ERR_SHAPE;
+  if (count > 0 && !d) return QLORA_ERR_NULL;
+  out->resize((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const qlora_linear_desc& x = d[i];
+    int st = check_linear_shape(T, x.K, x.N, r);
+    if (st != QLORA_OK) return st;
+    if (T > 0) {
+      if (!x.X || !x.codes || !x.q8 || !x.s2 || !x.A || !x.B || !x.Y || !x.XA) return QLORA_ERR_NULL;
+      if (!aligned16(x.X) || !aligned16(x.codes) || !aligned16(x.q8) || !aligned16(x.s2) || !aligned16(x.A) ||
+          !aligned16(x.B) || !aligned16(x.Y) || !aligned16(x.XA))
+        return QLORA_ERR_ALIGN;
+    }
+    (*out)[i] = qlora::GroupedLinear{x.X, x.codes, x.q8, x.s2, x.A, x.B, x.Y, x.XA, x.K, x.N};
+  }
+  return QLORA_OK;
+}
+}  // namespace
+
+size_t qlora_linear_fwd_grouped_workspace_bytes(int32_t count, const qlora_linear_desc* descs, int64_t T,
+                                                 int32_t r) {
+  // Only the shapes matter for the size; the pointers are not looked at.
+  if (count < 0 || count > 4096 || (count > 0 && !descs) || T < 0) return 0;
+  std::vector<qlora::GroupedLinear> g((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    if (check_linear_shape(T, descs[i].K, descs[i].N, r) != QLORA_OK) return 0;
+    g[i].K = descs[i].K;
+    g[i].N = descs[i].N;
+  }
+  return qlora::fwd_grouped_workspace_bytes(count, g.data(), T, r);
+}
+
+int qlora_linear_fwd_grouped(int32_t qtype, int32_t count, const qlora_linear_desc* descs, int64_t T, int32_t r,
+                             float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
+  if (T < 0) return QLORA_ERR_SHAPE;
+  std::vector<qlora::GroupedLinear> g;
+  int st = check_group(count, descs, T, r, &g);
+  if (st != QLORA_OK) return st;
+  if (T == 0 || count == 0) return QLORA_OK;
+  const size_t need = qlora::fwd_grouped_workspace_bytes(count, g.data(), T, r);
+  if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_linear_fwd_grouped(count, g.data(), T, r, (float)(alpha / (float)r), tt->cb,
+                                                     workspace, (hipStream_t)stream));
+}
+
+namespace {
+int check_group_bwd(int32_t count, const qlora_linear_bwd_desc* d, int64_t T, int32_t r,
+                    std::vector<qlora::GroupedLinearBwd>* out) {
+  if (count < 0 || count > 4096) return QLORA_ERR_SHAPE;
+  if (count > 0 && !d) return QLORA_ERR_NULL;
+  out->resize((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const qlora_linear_bwd_desc& x = d[i];
+    int st = check_linear_shape(T, x.K, x.N, r);
+    if (st != QLORA_OK) return st;
+    if (!x.dA || !x.dB) return QLORA_ERR_NULL;
+    if (!aligned16(x.dA) || !aligned16(x.dB)) return QLORA_ERR_ALIGN;
+    if (T > 0) {
+      if (!x.dY || !x.X || !x.XA || !x.codes || !x.q8 || !x.s2 || !x.A || !x.B || !x.dX) return QLORA_ERR_NULL;
+      if (!aligned16(x.dY) || !aligned16(x.X) || !aligned16(x.XA) || !aligned16(x.codes) || !aligned16(x.q8) ||
+          !aligned16(x.s2) || !aligned16(x.A) || !aligned16(x.B) || !aligned16(x.dX))
+        return QLORA_ERR_ALIGN;
+    }
+    (*out)[i] = qlora::GroupedLinearBwd{x.dY, x.X, x.XA, x.codes, x.q8, x.s2, x.A, x.B, x.dX, x.dA, x.dB, x.K, x.N};
+  }
+  return QLORA_OK;
+}
+}  // namespace
+
+size_t qlora_linear_bwd_grouped_workspace_bytes(int32_t count, const qlora_linear_bwd_desc* descs, int64_t T,
+                                                 int32_t r) {
+  if (count < 0 || count > 4096 || (count > 0 && !descs) || T < 0) return 0;
+  std::vector<qlora::GroupedLinearBwd> g((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    if (check_linear_shape(T, descs[i].K, descs[i].N, r) != QLORA_OK) return 0;
+    g[i].K = descs[i].K;
+    g[i].N = descs[i].N;
+  }
+  if (T == 0) return 0;
+  return qlora::bwd_grouped_workspace_bytes(count, g.data(), T, r);
+}
+
+int qlora_linear_bwd_grouped(int32_t qtype, int32_t count, const qlora_linear_bwd_desc* descs, int64_t T, int32_t r,
+                             float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+  const TypeTables* tt = type_tables(qtype);
+  if (!tt) return QLORA_ERR_UNSUPPORTED;
+  if (T < 0) return QLORA_ERR_SHAPE;
+  std::vector<qlora::GroupedLinearBwd> g;
+  int st = check_group_bwd(count, descs, T, r, &g);
+  if (st != QLORA_OK) return st;
+  if (count == 0) return QLORA_OK;
+  const size_t need = T > 0 ? qlora::bwd_grouped_workspace_bytes(count, g.data(), T, r) : 0;
+  if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_linear_bwd_grouped(count, g.data(), T, r, (float)(alpha / (float)r), tt->cb,
+                                                     workspace, (hipStream_t)stream));
 }
 
 int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes,

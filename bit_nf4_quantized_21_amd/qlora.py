@@ -19,6 +19,21 @@ _lib = None
 
 _c_i64, _c_i32, _c_p, _c_sz, _c_f = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 
+class LinearDesc(ctypes.Structure):
+    """qlora_linear_desc: one linear of a grouped forward (device pointers)."""
+    _fields_ = [("X", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("q8", ctypes.c_void_p),
+                ("s2", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("XA", ctypes.c_void_p), ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
+
+
+class LinearBwdDesc(ctypes.Structure):
+    """qlora_linear_bwd_desc: one linear of a grouped backward (device pointers)."""
+    _fields_ = [("dY", ctypes.c_void_p), ("X", ctypes.c_void_p), ("XA", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("q8", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("dX", ctypes.c_void_p), ("dA", ctypes.c_void_p),
+                ("dB", ctypes.c_void_p), ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
+
+
 _SIGNATURES = {
     "qlora_quantize_nf4": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
     "qlora_quantize_nf4_bf16": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p]),
@@ -44,6 +59,12 @@ _SIGNATURES = {
     "qlora_load_4bit_info": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64),
                                             ctypes.POINTER(_c_i64)]),
     "qlora_load_4bit": (ctypes.c_int, [ctypes.c_char_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "qlora_linear_fwd_grouped_workspace_bytes": (_c_sz, [_c_i32, ctypes.POINTER(LinearDesc), _c_i64, _c_i32]),
+    "qlora_linear_fwd_grouped": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(LinearDesc), _c_i64, _c_i32, _c_f,
+                                                _c_p, _c_sz, _c_p]),
+    "qlora_linear_bwd_grouped_workspace_bytes": (_c_sz, [_c_i32, ctypes.POINTER(LinearBwdDesc), _c_i64, _c_i32]),
+    "qlora_linear_bwd_grouped": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(LinearBwdDesc), _c_i64, _c_i32,
+                                                _c_f, _c_p, _c_sz, _c_p]),
     "qlora_timing_enable": (None, [ctypes.c_int]),
     "qlora_timing_read": (ctypes.c_int, [ctypes.c_char_p, _c_sz]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -313,6 +334,100 @@ def linear_fwd_noalloc(X, codes, q8, s2, A, B, alpha, N, Y, XA, stream=None):
     _check(lib().qlora_linear_fwd_noalloc(_p(X), T, K, N, _p(codes), _p(q8), _p(s2), _p(A), _p(B), r, float(alpha),
                                           _p(Y), _p(XA), _stream(stream)))
     return Y, XA
+
+
+def grouped_workspace_bytes(shapes, T, r, backward=False):
+    """Workspace bytes of a grouped forward (or backward) over linears of the
+    given (K, N) shapes."""
+    n = len(shapes)
+    if backward:
+        descs = (LinearBwdDesc * max(1, n))()
+        for i, (K, N) in enumerate(shapes):
+            descs[i].K, descs[i].N = K, N
+        return int(lib().qlora_linear_bwd_grouped_workspace_bytes(n, descs, T, r))
+    descs = (LinearDesc * max(1, n))()
+    for i, (K, N) in enumerate(shapes):
+        descs[i].K, descs[i].N = K, N
+    return int(lib().qlora_linear_fwd_grouped_workspace_bytes(n, descs, T, r))
+
+
+def linear_fwd_grouped(layers, alpha, T, r, workspace=None, stream=None, qtype="nf4"):
+    """Grouped forward of several linears that share T, r and alpha.
+
+    layers: list of dicts with X [T,K] bf16, codes, q8, s2, A [K,r], B [r,N]
+    and optionally Y [T,N] bf16 and XA [T,r] f32 (allocated when absent).
+    Returns the list of (Y, XA)."""
+    torch = _torch()
+    descs = (LinearDesc * max(1, len(layers)))()
+    outs = []
+    for i, L in enumerate(layers):
+        X, A, B = _dev(L["X"], torch.bfloat16, "X"), _dev(L["A"], torch.bfloat16, "A"), _dev(L["B"], torch.bfloat16, "B")
+        codes, q8, s2 = L["codes"], L["q8"], L["s2"]
+        _dev(codes, torch.uint8, "codes")
+        _dev(q8, torch.uint8, "q8")
+        _dev(s2, torch.float32, "s2")
+        if X.shape[0] != T or A.shape[1] != r or B.shape[0] != r or A.shape[0] != X.shape[1]:
+            raise ValueError("shape mismatch")
+        K, N = X.shape[1], B.shape[1]
+        _weight(codes, q8, s2, N, K)
+        Y = L.get("Y")
+        XA = L.get("XA")
+        Y = torch.empty(T, N, dtype=torch.bfloat16, device=X.device) if Y is None else Y
+        XA = torch.empty(T, r, dtype=torch.float32, device=X.device) if XA is None else XA
+        _need(_dev(Y, torch.bfloat16, "Y"), T * N, "Y")
+        _need(_dev(XA, torch.float32, "XA"), T * r, "XA")
+        descs[i] = LinearDesc(X.data_ptr(), codes.data_ptr(), q8.data_ptr(), s2.data_ptr(), A.data_ptr(),
+                              B.data_ptr(), Y.data_ptr(), XA.data_ptr(), K, N)
+        outs.append((Y, XA))
+    n = len(layers)
+    nbytes = int(lib().qlora_linear_fwd_grouped_workspace_bytes(n, descs, T, r))
+    dev = layers[0]["X"].device if layers else "cuda"
+    workspace = _workspace(nbytes, dev, workspace)
+    _check(lib().qlora_linear_fwd_grouped(_qtype(qtype), n, descs, T, r, float(alpha), _p(workspace), nbytes,
+                                          _stream(stream)))
+    return outs
+
+
+def linear_bwd_grouped(layers, alpha, T, r, workspace=None, stream=None, qtype="nf4"):
+    """Grouped backward of several linears that share T, r and alpha.
+
+    layers: list of dicts with dY [T,N], X [T,K], XA [T,r] (from the
+    forward), codes, q8, s2, A [K,r], B [r,N], and optionally dX, dA, dB
+    (allocated when absent).  Returns the list of (dX, dA, dB)."""
+    torch = _torch()
+    descs = (LinearBwdDesc * max(1, len(layers)))()
+    outs = []
+    for i, L in enumerate(layers):
+        dY, X = _dev(L["dY"], torch.bfloat16, "dY"), _dev(L["X"], torch.bfloat16, "X")
+        XA = _dev(L["XA"], torch.float32, "XA")
+        A, B = _dev(L["A"], torch.bfloat16, "A"), _dev(L["B"], torch.bfloat16, "B")
+        codes, q8, s2 = L["codes"], L["q8"], L["s2"]
+        _dev(codes, torch.uint8, "codes")
+        _dev(q8, torch.uint8, "q8")
+        _dev(s2, torch.float32, "s2")
+        K, N = X.shape[1], dY.shape[1]
+        if X.shape[0] != T or dY.shape[0] != T or A.shape != (K, r) or B.shape != (r, N) or XA.shape != (T, r):
+            raise ValueError("shape mismatch")
+        _weight(codes, q8, s2, N, K)
+        dX = L.get("dX")
+        dA = L.get("dA")
+        dB = L.get("dB")
+        dX = torch.empty(T, K, dtype=torch.bfloat16, device=X.device) if dX is None else dX
+        dA = torch.empty(K, r, dtype=torch.bfloat16, device=X.device) if dA is None else dA
+        dB = torch.empty(r, N, dtype=torch.bfloat16, device=X.device) if dB is None else dB
+        for t, nm, n in ((dX, "dX", T * K), (dA, "dA", K * r), (dB, "dB", r * N)):
+            _need(_dev(t, torch.bfloat16, nm), n, nm)
+        descs[i] = LinearBwdDesc(dY.data_ptr(), X.data_ptr(), XA.data_ptr(), codes.data_ptr(), q8.data_ptr(),
+                                 s2.data_ptr(), A.data_ptr(), B.data_ptr(), dX.data_ptr(), dA.data_ptr(),
+                                 dB.data_ptr(), K, N)
+        outs.append((dX, dA, dB))
+    n = len(layers)
+    nbytes = int(lib().qlora_linear_bwd_grouped_workspace_bytes(n, descs, T, r))
+    dev = layers[0]["X"].device if layers else "cuda"
+    workspace = _workspace(nbytes, dev, workspace)
+    _check(lib().qlora_linear_bwd_grouped(_qtype(qtype), n, descs, T, r, float(alpha), _p(workspace), nbytes,
+                                          _stream(stream)))
+    return outs
 
 
 def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None, workspace=None, stream=None,

@@ -200,6 +200,76 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Grouped forward: several frozen 4-bit linears with LoRA adapters that share
+ * the token count T, the rank r and alpha, in one call (fused q/k/v,
+ * gate/up, or every linear of a layer; the small-token path of 4-bit
+ * inference and batched generation, QLoRA project page, inference
+ * features).  Each linear computes exactly what qlora_linear_fwd_4bit
+ * computes for it.  For T <= 16, every run of up to 8 consecutive linears is
+ * one XA-partial launch and one dequant-GEMV launch over all their weights,
+ * so launch and ramp are paid once per run and the weight streams overlap
+ * (results bit for bit those of qlora_linear_fwd_4bit).  For larger T, every
+ * run of up to 4 consecutive linears with the same K and N (q/k/v, gate/up)
+ * shares one dequant-GEMM launch over all their output tiles, so small token
+ * counts fill the GPU with whole-contraction tiles; results equal
+ * qlora_linear_fwd_4bit's within the fp32 accumulation-order tolerance (the
+ * contraction may be cut into slices differently).
+ *   descs    host array of `count` linear descriptors (0 <= count <= 4096);
+ *            each names its own X [T,K], weight, A [K,r], B [r,N], and
+ *            outputs Y [T,N] and XA [T,r] (device pointers; several linears
+ *            may share one X).  K and N follow qlora_linear_fwd's rules.
+ *   workspace of at least qlora_linear_fwd_grouped_workspace_bytes bytes.
+ * Outputs of different linears must not overlap.
+ */
+typedef struct {
+  const uint16_t* X;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* Y;
+  float* XA;
+  int64_t K;
+  int64_t N;
+} qlora_linear_desc;
+size_t qlora_linear_fwd_grouped_workspace_bytes(int32_t count, const qlora_linear_desc* descs, int64_t T,
+                                                 int32_t r);
+int qlora_linear_fwd_grouped(int32_t qtype, int32_t count, const qlora_linear_desc* descs, int64_t T, int32_t r,
+                             float alpha, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped backward, the counterpart of qlora_linear_fwd_grouped: each linear
+ * gets what qlora_linear_bwd_4bit computes for it (dX, dA, dB); runs of up to
+ * 4 consecutive linears with the same K and N share one dX dequant-GEMM
+ * launch over all their tiles (dX within the accumulation-order tolerance of
+ * the single call; dA and dB bit for bit).  T = 0 zeroes every dA and dB.
+ *   descs  host array of `count` descriptors (0 <= count <= 4096), each with
+ *          its own dY [T,N], X [T,K], XA [T,r] (from the forward), weight,
+ *          A, B and outputs dX [T,K], dA [K,r], dB [r,N].
+ *   workspace of at least qlora_linear_bwd_grouped_workspace_bytes bytes.
+ */
+typedef struct {
+  const uint16_t* dY;
+  const uint16_t* X;
+  const float* XA;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* dX;
+  uint16_t* dA;
+  uint16_t* dB;
+  int64_t K;
+  int64_t N;
+} qlora_linear_bwd_desc;
+size_t qlora_linear_bwd_grouped_workspace_bytes(int32_t count, const qlora_linear_bwd_desc* descs, int64_t T,
+                                                 int32_t r);
+int qlora_linear_bwd_grouped(int32_t qtype, int32_t count, const qlora_linear_bwd_desc* descs, int64_t T, int32_t r,
+                             float alpha, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward without any device allocation, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same computation, kernels, arguments and results as

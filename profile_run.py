@@ -110,15 +110,15 @@ def run(workload, layers, steps):
     wl = dataclasses.replace(wl, layers=min(layers, wl.layers))
     lins = bench.linear_list(wl)
     weights, _ = bench.quantize_all(torch, qlora, synth, wl, lins)
-    Ls = bench.make_linears(torch, qlora, synth, wl, lins, weights)
+    Ls, groups = bench.make_linears(torch, qlora, synth, wl, lins, weights)
     del weights
     for _ in range(steps):
-        for L in Ls:
-            bench.run_fwd(qlora, L, wl.alpha)
-        for L in reversed(Ls):
-            bench.run_bwd(qlora, L, wl.alpha)
+        for g in groups:
+            bench.run_group_fwd(qlora, g, wl.alpha)
+        for g in reversed(groups):
+            bench.run_group_bwd(qlora, g, wl.alpha)
     torch.cuda.synchronize()
-    del Ls
+    del Ls, groups
     T, N, K = GEMV
     inp = synth.device_inputs(T, N, K, R, 0, backward=False)
     codes, absmax = qlora.quantize_nf4(inp["W"].view(-1))

@@ -203,3 +203,25 @@ def test_load_info_reads_a_safetensors_header(tmp_path):
         qlora.load_4bit_info(str(tmp_path / "junk"))
     with pytest.raises(qlora.QLoRAError):
         qlora.load_4bit_info(str(tmp_path / "missing"))
+
+
+def test_grouped_forward_argument_errors(L):
+    D = qlora.LinearDesc
+    descs = (D * 2)(D(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 4096, 4096),
+                    D(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 4096, 11008))
+    one = L.qlora_linear_fwd_workspace_bytes(4, 4096, 4096, 64) + L.qlora_linear_fwd_workspace_bytes(4, 4096, 11008, 64)
+    assert L.qlora_linear_fwd_grouped_workspace_bytes(2, descs, 4, 64) == one
+    assert L.qlora_linear_fwd_grouped_workspace_bytes(2, descs, 4, 12) == 0      # bad rank
+    assert L.qlora_linear_fwd_grouped_workspace_bytes(-1, descs, 4, 64) == 0
+    assert L.qlora_linear_fwd_grouped(3, 2, descs, 4, 64, 16.0, P, 1 << 30, None) == EUNSUP
+    assert L.qlora_linear_fwd_grouped(0, 2, descs, 4, 64, 16.0, P, one - 1, None) == EWS
+    assert L.qlora_linear_fwd_grouped(0, 2, None, 4, 64, 16.0, P, 1 << 30, None) == ENULL
+    assert L.qlora_linear_fwd_grouped(0, 0, None, 4, 64, 16.0, None, 0, None) == OK
+    assert L.qlora_linear_fwd_grouped(0, 2, descs, 0, 64, 16.0, None, 0, None) == OK
+    descs[1].K = 100
+    assert L.qlora_linear_fwd_grouped(0, 2, descs, 4, 64, 16.0, P, 1 << 30, None) == ESHAPE
+    descs[1].K = 11008
+    descs[0].Y = 0x10004
+    assert L.qlora_linear_fwd_grouped(0, 2, descs, 4, 64, 16.0, P, 1 << 30, None) == EALIGN
+    descs[0].Y = 0
+    assert L.qlora_linear_fwd_grouped(0, 2, descs, 4, 64, 16.0, P, 1 << 30, None) == ENULL

@@ -1,0 +1,96 @@
+"""GPU parity of the grouped small-token forward: every linear of a group
+gets exactly (bit for bit) what the single-linear forward gives it, across
+group sizes (including more linears than one launch holds), shared inputs,
+ragged shapes and the GEMM fallback for larger T; and a ragged group is
+checked against the oracle directly."""
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_21_amd import synth
+from oracle import compare, lora, nf4
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _q():
+    from bit_nf4_quantized_21_amd import qlora
+    return qlora
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _make(shapes, T, r, shared_x=False, seed0=0):
+    q = _q()
+    layers = []
+    xs = {}
+    for i, (N, K) in enumerate(shapes):
+        seed = seed0 + i
+        W = torch.from_numpy(synth.weight(N, K, seed).ravel()).cuda()
+        codes, q8, s2 = q.quantize_dq(W)
+        key = K if shared_x else (K, i)
+        if key not in xs:
+            xs[key] = _bf16_dev(synth.x_bits(T, K, seed))
+        layers.append(dict(X=xs[key], codes=codes, q8=q8, s2=s2, A=_bf16_dev(synth.a_bits(K, r, seed)),
+                           B=_bf16_dev(synth.b_bits(r, N, seed)), N=N, K=K, seed=seed))
+    return layers
+
+
+LLAMA7B = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_grouped_7b_layer_matches_single(T):
+    """All seven linears of a LLaMA-7B layer (q, k, v, o share nothing here;
+    gate and up share X) in one grouped call."""
+    print(f"grouped 7b layer T={T}", flush=True)
+    q = _q()
+    layers = _make(LLAMA7B, T, 64, shared_x=True, seed0=100 + T)
+    outs = q.linear_fwd_grouped(layers, 16.0, T, 64)
+    for L, (Y, XA) in zip(layers, outs):
+        Y1, XA1 = q.linear_fwd(L["X"], L["codes"], L["q8"], L["s2"], L["A"], L["B"], 16.0, L["N"])
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16)), (L["N"], L["K"])
+        assert torch.equal(XA.view(torch.int32), XA1.view(torch.int32)), (L["N"], L["K"])
+
+
+@pytest.mark.parametrize("count,T,r", [(11, 3, 8), (9, 16, 128), (3, 64, 64), (1, 7, 72)])
+def test_grouped_sizes_and_fallback(count, T, r):
+    """More linears than one launch serves (11 and 9 -> two launches), the
+    widest rank, ragged N, and T > 16 (each linear on the GEMM path)."""
+    print(f"grouped count={count} T={T} r={r}", flush=True)
+    q = _q()
+    shapes = [((8 * (97 + 13 * i)) % 2048 + 8, 64 * (1 + (5 * i) % 23)) for i in range(count)]
+    layers = _make(shapes, T, r, seed0=200 + count)
+    outs = q.linear_fwd_grouped(layers, 16.0, T, r)
+    for L, (Y, XA) in zip(layers, outs):
+        Y1, XA1 = q.linear_fwd(L["X"], L["codes"], L["q8"], L["s2"], L["A"], L["B"], 16.0, L["N"])
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16)), (L["N"], L["K"])
+        assert torch.equal(XA.view(torch.int32), XA1.view(torch.int32)), (L["N"], L["K"])
+
+
+def test_grouped_ragged_against_oracle():
+    q = _q()
+    T, r, alpha = 5, 16, 16.0
+    shapes = [(520, 640), (776, 1024), (24, 64), (1000, 2048)]
+    layers = _make(shapes, T, r, seed0=300)
+    outs = q.linear_fwd_grouped(layers, alpha, T, r)
+    torch.cuda.synchronize()
+    for L, (Y, XA) in zip(layers, outs):
+        N, K, seed = L["N"], L["K"], L["seed"]
+        codes, q8, s2, _ = nf4.quantize_all(synth.weight(N, K, seed))
+        Wd = nf4.dequantize(codes, q8, s2, N * K, "bf16").reshape(N, K)
+        X = nf4.bf16_bits_to_f32(synth.x_bits(T, K, seed))
+        A = nf4.bf16_bits_to_f32(synth.a_bits(K, r, seed))
+        B = nf4.bf16_bits_to_f32(synth.b_bits(r, N, seed))
+        Yr, XAr = lora.linear_fwd(X, Wd, A, B, alpha, r)
+        ok, info = compare.check_close(Y.float().cpu().numpy().astype(np.float64), Yr)
+        assert ok, (N, K, info)
+        # XA: fp32 accumulation of K exact bf16 products
+        bound = 2 * K * 2.0 ** -24 * (np.abs(X.astype(np.float64)) @ np.abs(A.astype(np.float64))) + 1e-30
+        assert np.all(np.abs(XA.cpu().numpy().astype(np.float64) - XAr) <= bound), (N, K)
