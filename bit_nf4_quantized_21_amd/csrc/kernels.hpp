@@ -80,4 +80,11 @@ hipError_t launch_linear_fwd_grouped(int count, const GroupedLinear* L, int64_t 
 hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint16_t* dY, const uint16_t* X,
                              const float* XA, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, hipStream_t s);
 
+// AdamW update of a flat adapter buffer (optim.hip); `ws` holds the fp64
+// norm partials when clipping or the norm is asked for.
+size_t adamw_workspace_bytes(int64_t n);
+hipError_t launch_adamw(int64_t n, uint16_t* param, float* master, float* m, float* v, const uint16_t* grad,
+                        int32_t step, float lr, float b1, float b2, float eps, float wd, float max_norm,
+                        float* norm_out, void* ws, hipStream_t s);
+
 }  // namespace qlora

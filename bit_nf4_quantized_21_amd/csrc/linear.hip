@@ -56,7 +56,7 @@ int64_t tok_chunk(int64_t T, int64_t C) {
 
 // Backward workspace regions, each 256-byte aligned.
 struct BwdLayout {
-  size_t pg, g, planes, ptok_b, ptok_a, slots, counters, total;
+  size_t pg, g, planes, ptok_b, ptok_a, slots, counters, xa, pxa, total;
 };
 BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   BwdLayout l{};
@@ -71,7 +71,11 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
   const SplitPlan dp = dx_plan(T, K, N);
   l.slots = dp.S > 1 ? align256((size_t)dp.nsplit() * dp.S * kSplitSlotFloats * sizeof(float)) : 0;
   l.counters = align256((size_t)(dp.nsplit() > 0 ? 2 * dp.nsplit() : 1) * sizeof(int));
-  l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok_b + l.ptok_a + l.slots + l.counters;
+  // recomputation of XA when the caller did not keep it: XA and its rowdot
+  // partials
+  l.xa = align256((size_t)T * r * sizeof(float));
+  l.pxa = align256((size_t)cdiv(K, row_chunk(T, K)) * T * RP * sizeof(float));
+  l.total = l.pg + 2 * l.g + 4 * l.planes + l.ptok_b + l.ptok_a + l.slots + l.counters + l.xa + l.pxa;
   return l;
 }
 }  // namespace
@@ -451,6 +455,18 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   int* counters = reinterpret_cast<int*>(w3 + l.slots);
   const SplitPlan dp = dx_plan(a.T, a.K, a.N);
   const int64_t TP = round_up(a.T, 64);
+  if (!XA) {
+    // Gradient checkpointing: the forward's XA was not kept, so recompute
+    // it from X and A (the same kernels and order as the forward, so the
+    // value is the forward's bit for bit).
+    float* xa = reinterpret_cast<float*>(w3 + l.slots + l.counters);
+    RowdotOut ox{};
+    ox.f32 = xa;
+    hipError_t e0 = launch_rowdot(X, a.A, /*v_lr=*/true, reinterpret_cast<float*>(w3 + l.slots + l.counters + l.xa),
+                                  ox, a.T, a.K, a.r, row_chunk(a.T, a.K), s);
+    if (e0 != hipSuccess) return e0;
+    XA = xa;
+  }
 
   // G = dY B^T as the bf16 hi / lo rows of s G (the dX GEMM's adapter step)
   // and as transposed hi / lo planes (dA), plus the planes of XA (dB).

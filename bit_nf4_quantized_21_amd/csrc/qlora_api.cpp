@@ -363,6 +363,56 @@ int qlora_linear_bwd_grouped(int32_t qtype, int32_t count, const qlora_linear_bw
                                                      workspace, (hipStream_t)stream));
 }
 
+namespace {
+// The device address of a buffer given as device memory or as pinned host
+// memory mapped into the device's address space; nullptr if it is neither.
+void* device_view(void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice) return p;
+  if (at.type == hipMemoryTypeHost) {
+    if (at.devicePointer) return at.devicePointer;
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+}  // namespace
+
+size_t qlora_adamw_workspace_bytes(int64_t n) { return n > 0 ? qlora::adamw_workspace_bytes(n) : 0; }
+
+int qlora_adamw_step(int64_t n, uint16_t* param, float* master, float* m, float* v, const uint16_t* grad,
+                     int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                     float max_grad_norm, float* grad_norm_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (n < 0 || step < 1) return QLORA_ERR_SHAPE;
+  if (!(lr >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+      !(weight_decay >= 0.0f) || !std::isfinite(lr) || !std::isfinite(max_grad_norm))
+    return QLORA_ERR_UNSUPPORTED;
+  if (n == 0) return QLORA_OK;
+  if (!param || !master || !m || !v || !grad) return QLORA_ERR_NULL;
+  if (!aligned16(param) || !aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(grad) ||
+      (grad_norm_out && (reinterpret_cast<uintptr_t>(grad_norm_out) & 3u)))
+    return QLORA_ERR_ALIGN;
+  const bool need_ws = max_grad_norm > 0.0f || grad_norm_out;
+  if (need_ws && (!workspace || workspace_bytes < qlora::adamw_workspace_bytes(n))) return QLORA_ERR_WORKSPACE;
+  if (need_ws && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  // Optimizer state may be paged out to pinned host memory.
+  float* dm = static_cast<float*>(device_view(master));
+  float* d1 = static_cast<float*>(device_view(m));
+  float* d2 = static_cast<float*>(device_view(v));
+  if (!dm || !d1 || !d2) return QLORA_ERR_UNSUPPORTED;
+  return hip_status(qlora::launch_adamw(n, param, dm, d1, d2, grad, step, lr, beta1, beta2, eps, weight_decay,
+                                        max_grad_norm, grad_norm_out, workspace, (hipStream_t)stream));
+}
+
 int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
                              const uint8_t* q8, const float* s2, const uint16_t* A, const uint16_t* B, int32_t r,
                              float alpha, uint16_t* Y, float* XA, void* stream) {
@@ -390,7 +440,7 @@ int qlora_linear_bwd_4bit(int32_t qtype, const uint16_t* dY, const uint16_t* X, 
   int st = check_linear_shape(T, K, N, r);
   if (st != QLORA_OK) return st;
   if (!dA || !dB) return QLORA_ERR_NULL;
-  if (T > 0 && (!dY || !X || !XA || !codes || !q8 || !s2 || !A || !B || !dX)) return QLORA_ERR_NULL;
+  if (T > 0 && (!dY || !X || !codes || !q8 || !s2 || !A || !B || !dX)) return QLORA_ERR_NULL;  // XA may be NULL
   if (!aligned16(dA) || !aligned16(dB)) return QLORA_ERR_ALIGN;
   if (T > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(XA) || !aligned16(codes) || !aligned16(q8) ||
                 !aligned16(s2) || !aligned16(A) || !aligned16(B) || !aligned16(dX)))

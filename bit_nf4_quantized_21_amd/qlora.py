@@ -65,6 +65,9 @@ _SIGNATURES = {
     "qlora_linear_bwd_grouped_workspace_bytes": (_c_sz, [_c_i32, ctypes.POINTER(LinearBwdDesc), _c_i64, _c_i32]),
     "qlora_linear_bwd_grouped": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(LinearBwdDesc), _c_i64, _c_i32,
                                                 _c_f, _c_p, _c_sz, _c_p]),
+    "qlora_adamw_workspace_bytes": (_c_sz, [_c_i64]),
+    "qlora_adamw_step": (ctypes.c_int, [_c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_f, _c_f, _c_f, _c_f, _c_f,
+                                        _c_f, _c_p, _c_p, _c_sz, _c_p]),
     "qlora_timing_enable": (None, [ctypes.c_int]),
     "qlora_timing_read": (ctypes.c_int, [ctypes.c_char_p, _c_sz]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -436,7 +439,8 @@ def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None,
     torch = _torch()
     _dev(dY, torch.bfloat16, "dY")
     _dev(X, torch.bfloat16, "X")
-    _dev(XA, torch.float32, "XA")
+    if XA is not None:                 # None: recomputed from X and A (gradient checkpointing)
+        _dev(XA, torch.float32, "XA")
     _dev(A, torch.bfloat16, "A")
     _dev(B, torch.bfloat16, "B")
     _dev(codes, torch.uint8, "codes")
@@ -445,7 +449,7 @@ def linear_bwd(dY, X, XA, codes, q8, s2, A, B, alpha, dX=None, dA=None, dB=None,
     T, K = X.shape
     N = dY.shape[1]
     r = A.shape[1]
-    if A.shape != (K, r) or B.shape != (r, N) or dY.shape[0] != T or XA.shape != (T, r):
+    if A.shape != (K, r) or B.shape != (r, N) or dY.shape[0] != T or (XA is not None and XA.shape != (T, r)):
         raise ValueError("shape mismatch")
     _weight(codes, q8, s2, N, K)
     dX = torch.empty(T, K, dtype=torch.bfloat16, device=X.device) if dX is None else dX
@@ -491,3 +495,33 @@ def load_4bit(path, device="cuda", stream=None):
     _check(lib().qlora_load_4bit(os.fsencode(path), _qtype(qtype), N, K, _p(codes), _p(q8), _p(s2),
                                  _stream(stream)))
     return codes, q8, s2, qtype, N, K
+
+
+def adamw_workspace_bytes(n):
+    return int(lib().qlora_adamw_workspace_bytes(n))
+
+
+def adamw_step(param, master, m, v, grad, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+               max_grad_norm=0.0, grad_norm_out=None, workspace=None, stream=None):
+    """One AdamW step over flat adapter buffers (see qlora_adamw_step).
+
+    param, grad: bf16 CUDA tensors; master, m, v: fp32 tensors on the GPU or
+    in pinned host memory (paged optimizer state).  grad_norm_out: optional
+    fp32 CUDA tensor of one element."""
+    torch = _torch()
+    n = param.numel()
+    _need(_dev(param, torch.bfloat16, "param"), n, "param")
+    _need(_dev(grad, torch.bfloat16, "grad"), n, "grad")
+    for t, nm in ((master, "master"), (m, "m"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous float32 tensor")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{nm} must be on the GPU or in pinned host memory")
+        _need(t, n, nm)
+    if grad_norm_out is not None:
+        _dev(grad_norm_out, torch.float32, "grad_norm_out")
+    nbytes = adamw_workspace_bytes(n)
+    workspace = _workspace(nbytes, param.device, workspace)
+    _check(lib().qlora_adamw_step(n, _p(param), _p(master), _p(m), _p(v), _p(grad), int(step), float(lr),
+                                  float(beta1), float(beta2), float(eps), float(weight_decay), float(max_grad_norm),
+                                  _p(grad_norm_out), _p(workspace), nbytes, _stream(stream)))

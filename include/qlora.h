@@ -298,7 +298,11 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t T, int64_t K, int64_t N,
  *     dA = s X^T G                        (bf16)
  *     dB = s (XA)^T dY                    (bf16)
  *   dY [T,N] bf16 upstream gradient; X [T,K] the forward input; XA [T,r] the
- *   fp32 buffer qlora_linear_fwd wrote for this X and A.  Other arguments as
+ *   fp32 buffer qlora_linear_fwd wrote for this X and A, or NULL when the
+ *   caller did not keep it (gradient checkpointing, QLoRA project page, core
+ *   techniques: activations are recomputed instead of stored): XA is then
+ *   recomputed from X and A inside the call (bit for bit the forward's for
+ *   T > 16; within fp32 accumulation order for T <= 16).  Other arguments as
  *   in qlora_linear_fwd.  dX [T,K], dA [K,r], dB [r,N] are overwritten.
  *   T = 0 is allowed: dX is empty and dA, dB are set to zero.
  *   workspace of at least qlora_linear_bwd_workspace_bytes(T,K,N,r) bytes.
@@ -312,6 +316,40 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const float* XA,
                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                      uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One AdamW step over a flat buffer of adapter parameters (QLoRA project
+ * page, technical architecture: the adapters are trained with AdamW and
+ * paged optimizers; challenges: gradient clipping keeps training stable).
+ * With g = c * grad and t = step (1, 2, ...):
+ *     m = b1 m + (1-b1) g,   v = b2 v + (1-b2) g^2,
+ *     master = master - lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd master),
+ *     param = bf16(master)   (round to nearest even)
+ * where c = min(1, max_grad_norm / (||grad|| + 1e-6)) with ||grad|| the L2
+ * norm of the whole buffer (c = 1 when max_grad_norm <= 0).  The adapters of
+ * all linears are meant to live in one flat allocation (per-linear views),
+ * so one call updates them all.
+ *   n                 elements (>= 0; 0 = no-op).
+ *   param   [n] bf16  in/out: the adapter values the layer uses.
+ *   master  [n] fp32  in/out: master copy of the parameters.
+ *   m, v    [n] fp32  in/out: first and second moments (zero before step 1).
+ *   grad    [n] bf16  the gradients (dA, dB of qlora_linear_bwd).
+ *   grad_norm_out     optional device float: receives ||grad|| (unclipped).
+ *   workspace         qlora_adamw_workspace_bytes(n) bytes when clipping or
+ *                     grad_norm_out is asked for (else may be NULL).
+ * Paged optimizer: master, m and v may be device memory or pinned host
+ * memory (hipHostMalloc, e.g. torch pin_memory tensors); the state then takes
+ * no GPU memory and the step streams it over the host link.  Pageable host
+ * memory returns QLORA_ERR_UNSUPPORTED.  The norm is summed in fp64 in a
+ * fixed order, so results are deterministic.  Hyperparameters must satisfy
+ * 0 <= b1, b2 < 1, eps > 0, lr >= 0, wd >= 0 (else QLORA_ERR_UNSUPPORTED);
+ * step < 1 returns QLORA_ERR_SHAPE.
+ */
+size_t qlora_adamw_workspace_bytes(int64_t n);
+int qlora_adamw_step(int64_t n, uint16_t* param, float* master, float* m, float* v, const uint16_t* grad,
+                     int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                     float max_grad_norm, float* grad_norm_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * Support: dequantize codes + double-quantized constants to a dense weight.
