@@ -24,12 +24,21 @@ Beside it, in the same JSON line:
                 rotating weight copies (> 390 MB of codes: cold HBM);
   quantize      11008x4096 weights (fp32 and bf16) over 40 rotating source
                 copies, median per-launch event time;
+  gemv_grouped  the seven linears of a LLaMA-7B layer in one grouped
+                small-token call (4 tokens), rotating over 4 layer copies;
+  optimizer     AdamW with clipping over all 800 M adapter parameters of the
+                65B set (state in HBM) and, paged, over one layer's (state in
+                pinned host memory);
   peaks         the copy and bf16-MFMA rates this GPU sustains (probes), with
                 the headline fractions against them;
   cpu_baseline  the CPU oracle on a bounded sample, per stage, median of 3.
 
     python bench.py [--steps K] [--warmup W] [--workload full65b|layer33b|mlp7b|tiny]
-                    [--no-extras] [--no-cpu-baseline]
+                    [--no-extras] [--no-cpu-baseline] [--legs workloads,gemv,...]
+
+q, k, v and gate, up (same shape, the same input in a LLaMA block) run as
+batched launches, the other linears alone; each linear keeps its own inputs
+and outputs.
 """
 
 from __future__ import annotations
@@ -200,8 +209,15 @@ def make_linears(torch, qlora, synth, wl, lins, weights):
     Ybuf = [torch.empty(T * maxN, dtype=torch.bfloat16, device="cuda") for _ in range(width)]
     dXbuf = [torch.empty(T * maxK, dtype=torch.bfloat16, device="cuda") for _ in range(width)]
     shapes = {tuple((L["K"], L["N"]) for L in g) for g in groups}
-    wsf = max(qlora.grouped_workspace_bytes(list(sh), T, r) for sh in shapes)
-    wsb = max(qlora.grouped_workspace_bytes(list(sh), T, r, backward=True) for sh in shapes)
+    wsf = wsb = 0
+    for sh in shapes:
+        if len(sh) == 1:   # a single linear runs through linear_fwd / linear_bwd
+            (K, N), = sh
+            wsf = max(wsf, qlora.linear_fwd_workspace_bytes(T, K, N, r))
+            wsb = max(wsb, qlora.linear_bwd_workspace_bytes(T, K, N, r))
+        else:
+            wsf = max(wsf, qlora.grouped_workspace_bytes(list(sh), T, r))
+            wsb = max(wsb, qlora.grouped_workspace_bytes(list(sh), T, r, backward=True))
     wsf = torch.empty(max(1, wsf), dtype=torch.uint8, device="cuda")
     wsb = torch.empty(max(1, wsb), dtype=torch.uint8, device="cuda")
     for g in groups:
@@ -490,6 +506,43 @@ def bench_quantize(torch, qlora, copies=40, reps=80):
     return res
 
 
+def bench_optimizer(torch, qlora, synth):
+    """AdamW with global-norm clipping over the adapters of the whole 65B set
+    (r = 64 on all 560 linears: 800 M parameters in one flat buffer), state
+    in HBM; and the paged mode (state in pinned host memory) on one layer's
+    adapters.  Median of 5 event-timed steps each."""
+    wl = synth.WORKLOADS["full65b"]
+    res = {}
+    for label, layers, paged in (("device_state", wl.layers, False), ("paged_state", 1, True)):
+        n = sum(wl.r * (l.K + l.N) for l in wl.linears) * layers
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        param = (torch.randn(n, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+        grad = torch.randn(n, generator=g, device="cuda").to(torch.bfloat16)
+        master = param.float()
+        m = torch.zeros(n, device="cuda")
+        v = torch.zeros(n, device="cuda")
+        if paged:
+            master, m, v = (x.cpu().pin_memory() for x in (master, m, v))
+        ws = torch.empty(max(1, qlora.adamw_workspace_bytes(n)), dtype=torch.uint8, device="cuda")
+        steps = iter(range(1, 100))
+        qlora.adamw_step(param, master, m, v, grad, next(steps), 1e-4, max_grad_norm=1.0, workspace=ws)
+        us = _event_median(torch, lambda _: qlora.adamw_step(param, master, m, v, grad, next(steps), 1e-4,
+                                                              max_grad_norm=1.0, workspace=ws), [0], 5)
+        # grad read twice (norm, update), param written, master/m/v read and written
+        nbytes = n * (2 * 2 + 2 + 3 * 8)
+        res[label] = {"params": n, "median_us": round(us, 1), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "bytes": nbytes}
+        if not paged:
+            res[label]["frac_hbm"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        else:
+            res[label]["note"] = "master, m, v (24 B/param) cross the host link each step"
+        del param, grad, master, m, v, ws
+        torch.cuda.empty_cache()
+    res["workload"] = "AdamW + global-norm clipping over the LoRA adapters (r=64) of the 65B set"
+    return res
+
+
 def measure_peaks(torch):
     """The copy bandwidth and bf16 MFMA rate this GPU sustains (probes in
     bench_peaks.so), medians of 5 event-timed launches."""
@@ -603,7 +656,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="headline workload only (no other workloads, GEMV, quantize or peak probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="workloads,gemv,gemv_grouped,quantize,peaks",
+    ap.add_argument("--legs", default="workloads,gemv,gemv_grouped,quantize,optimizer,peaks",
                     help="extra legs to run after the headline (comma list)")
     ap.add_argument("--skip-headline", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -658,6 +711,12 @@ def main():
     if "quantize" in legs:
         print("bench: quantize", file=sys.stderr, flush=True)
         out["quantize"] = bench_quantize(torch, qlora)
+    if "optimizer" in legs:
+        print("bench: optimizer", file=sys.stderr, flush=True)
+        out["optimizer"] = bench_optimizer(torch, qlora, synth)
+        if "ms_per_step" in out:
+            out["optimizer"]["headline_step_with_optimizer_ms"] = round(
+                out["ms_per_step"] + out["optimizer"]["device_state"]["median_us"] / 1e3, 3)
     if "peaks" in legs:
         print("bench: peaks", file=sys.stderr, flush=True)
         peaks = measure_peaks(torch)

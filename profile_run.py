@@ -101,6 +101,29 @@ def workload_shapes(workload):
     return wl.T, [(l.N, l.K) for l in wl.linears]
 
 
+def launches_per_layer(workload):
+    """GEMM launches per layer: the step batches q/k/v and gate/up."""
+    import bench
+    from bit_nf4_quantized_21_amd import synth
+    names = [l.name for l in synth.WORKLOADS[workload].linears]
+    n = 0
+    for i, nm in enumerate(names):
+        prev = names[i - 1] if i else None
+        if not (prev and any(nm in fs and prev in fs for fs in bench.FUSED_SETS)):
+            n += 1
+    return n
+
+
+def per_launch(values, workload, kernel):
+    """Algorithmic work per launch of a GEMM (a launch covers a batch of
+    linears) or of a per-linear kernel."""
+    if values[0] is None:
+        return None
+    if kernel in ("gemm_fwd_kernel", "gemm_dx_kernel"):
+        return sum(values) / launches_per_layer(workload)
+    return sum(values) / len(values)
+
+
 def run(workload, layers, steps):
     import torch
     import bench
@@ -183,10 +206,9 @@ def traffic(fetch_dir, write_dir, command, workload):
         fb = sum(f) / len(f) * 1024 / ff
         wb = sum(w) / len(w) * 1024 / wf
         if wl == workload:
-            alg = [algorithmic_bytes(kernel, T_w, N, K, R) for (N, K) in shapes]
+            alg_b = per_launch([algorithmic_bytes(kernel, T_w, N, K, R) for (N, K) in shapes], workload, kernel)
         else:
-            alg = [algorithmic_bytes(kernel, *GEMV, R)]
-        alg_b = None if alg[0] is None else sum(alg) / len(alg)
+            alg_b = algorithmic_bytes(kernel, *GEMV, R)
         rec = {"kernel": kernel, "workload": wl, "launches": len(f), "fetch_bytes_per_launch": round(fb),
                "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb),
                "algorithmic_bytes_per_launch": alg_b, "copy_factor_fetch": round(ff, 5),
@@ -237,10 +259,10 @@ def mfma(pmc_dir, command, workload):
         wl = "gemv7b" if ("gemv" in kernel or "xa_" in kernel) else workload
         T_w, shapes = workload_shapes(workload)
         if wl == workload:
-            alg = [algorithmic_flops(kernel, T_w, N, K, R) for (N, K) in shapes]
+            alg = per_launch([algorithmic_flops(kernel, T_w, N, K, R) for (N, K) in shapes], workload, kernel)
         else:
-            alg = [algorithmic_flops(kernel, *GEMV, R)]
-        algs = "" if alg[0] is None else f"{sum(alg) / len(alg) / 1e9:.1f}"
+            alg = algorithmic_flops(kernel, *GEMV, R)
+        algs = "" if alg is None else f"{alg / 1e9:.1f}"
         fs = f"{sum(f) / len(f) / 1e9:.1f}" if f else ""
         lines.append(f"| {kernel} | {wl} | {len(u)} | {sum(u) / len(u):.1f} | {fs} | {algs} |")
     os.makedirs(PROFILES, exist_ok=True)
