@@ -192,11 +192,12 @@ FwdBatchLayout fwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int 
   l.g = fwd_plan(T, K, N, count);
   l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
   l.counters = align256((size_t)(l.g.nsplit() > 0 ? 2 * l.g.nsplit() : 1) * sizeof(int));
-  l.total = l.p + 2 * (size_t)count * l.xah + l.slots + l.counters;
+  // per problem: rowdot partials and the hi / lo rows of s XA
+  l.total = (size_t)count * (l.p + 2 * l.xah) + l.slots + l.counters;
   return l;
 }
 struct BwdBatchLayout {
-  size_t pg, g, planes, ptok_b, ptok_a, slots, counters, total;
+  size_t pg, g, planes, ptok_b, ptok_a, per, slots, counters, total;
   SplitPlan d;
 };
 BwdBatchLayout bwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
@@ -210,7 +211,10 @@ BwdBatchLayout bwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int 
   l.d = dx_plan(T, K, N, count);
   l.slots = l.d.S > 1 ? align256((size_t)l.d.nsplit() * l.d.S * kSplitSlotFloats * sizeof(float)) : 0;
   l.counters = align256((size_t)(l.d.nsplit() > 0 ? 2 * l.d.nsplit() : 1) * sizeof(int));
-  l.total = l.pg + 2 * (size_t)count * l.g + 4 * l.planes + l.ptok_b + l.ptok_a + l.slots + l.counters;
+  // per problem: rowdot partials, hi / lo rows of s G, four tokdot planes
+  // and the two tokdot partial areas
+  l.per = l.pg + 2 * l.g + 4 * l.planes + l.ptok_b + l.ptok_a;
+  l.total = (size_t)count * l.per + l.slots + l.counters;
   return l;
 }
 }  // namespace
@@ -229,30 +233,34 @@ hipError_t launch_linear_fwd_batch(int count, const GroupedLinear* L, int64_t T,
   const int64_t K = L[0].K, N = L[0].N;
   const FwdBatchLayout l = fwd_batch_layout(T, K, N, r, count);
   char* w = reinterpret_cast<char*>(ws);
-  float* P = reinterpret_cast<float*>(w);
-  char* wx = w + l.p;
-  char* w2 = wx + 2 * (size_t)count * l.xah;
+  char* w2 = w + (size_t)count * (l.p + 2 * l.xah);
   int* counters = reinterpret_cast<int*>(w2 + l.slots);
   FwdGemmParams p{};
   hipError_t e = hipSuccess;
   p.status = status_word(&e);
   if (!p.status) return e;
+  // XA = X A of every problem: one launch of each rowdot kernel
+  const uint16_t* Ms[kRowdotJobsMax];
+  const uint16_t* Vs[kRowdotJobsMax];
+  float* Ps[kRowdotJobsMax];
+  RowdotOut os[kRowdotJobsMax] = {};
   for (int i = 0; i < count; ++i) {
-    uint16_t* XAh = reinterpret_cast<uint16_t*>(wx + (2 * (size_t)i) * l.xah);
-    uint16_t* XAl = reinterpret_cast<uint16_t*>(wx + (2 * (size_t)i + 1) * l.xah);
-    RowdotOut o{};
-    o.f32 = L[i].XA;
-    o.row_hi = XAh;
-    o.row_lo = XAl;
-    o.scale_row = s;
-    if (i == 0) {
-      o.zero = counters;  // the batched GEMM's split tickets
-      o.nzero = 2 * l.g.nsplit();
-    }
-    e = launch_rowdot(L[i].X, L[i].A, /*v_lr=*/true, P, o, T, K, r, row_chunk(T, K), st);
-    if (e != hipSuccess) return e;
+    char* wi = w + (size_t)i * (l.p + 2 * l.xah);
+    uint16_t* XAh = reinterpret_cast<uint16_t*>(wi + l.p);
+    uint16_t* XAl = reinterpret_cast<uint16_t*>(wi + l.p + l.xah);
+    Ms[i] = L[i].X;
+    Vs[i] = L[i].A;
+    Ps[i] = reinterpret_cast<float*>(wi);
+    os[i].f32 = L[i].XA;
+    os[i].row_hi = XAh;
+    os[i].row_lo = XAl;
+    os[i].scale_row = s;
     p.prob[i] = FwdGemmProblem{L[i].X, L[i].codes, L[i].q8, L[i].s2, L[i].B, XAh, XAl, L[i].Y};
   }
+  os[0].zero = counters;  // the batched GEMM's split tickets
+  os[0].nzero = 2 * l.g.nsplit();
+  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/true, Ps, os, T, K, r, row_chunk(T, K), st);
+  if (e != hipSuccess) return e;
   p.batch = count;
   p.T = T;
   p.K = K;
@@ -279,26 +287,31 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
   }
   const BwdBatchLayout l = bwd_batch_layout(T, K, N, r, count);
   char* w = reinterpret_cast<char*>(ws);
-  float* Pg = reinterpret_cast<float*>(w);
-  char* wg = w + l.pg;
-  char* w2 = wg + 2 * (size_t)count * l.g;
-  uint16_t* Gth = reinterpret_cast<uint16_t*>(w2);
-  uint16_t* Gtl = reinterpret_cast<uint16_t*>(w2 + l.planes);
-  uint16_t* XAth = reinterpret_cast<uint16_t*>(w2 + 2 * l.planes);
-  uint16_t* XAtl = reinterpret_cast<uint16_t*>(w2 + 3 * l.planes);
-  float* Ptok_b = reinterpret_cast<float*>(w2 + 4 * l.planes);
-  float* Ptok_a = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok_b);
-  char* w3 = w2 + 4 * l.planes + l.ptok_b + l.ptok_a;
+  char* w3 = w + (size_t)count * l.per;
   int* counters = reinterpret_cast<int*>(w3 + l.slots);
   const int64_t TP = round_up(T, 64);
   DxGemmParams p{};
   hipError_t e = hipSuccess;
   p.status = status_word(&e);
   if (!p.status) return e;
+  const uint16_t* Ms[kRowdotJobsMax];
+  const uint16_t* Vs[kRowdotJobsMax];
+  float* Ps[kRowdotJobsMax];
+  RowdotOut os[kRowdotJobsMax] = {};
+  TokJob tj[2 * kRowdotJobsMax] = {};
   for (int i = 0; i < count; ++i) {
-    uint16_t* Gh = reinterpret_cast<uint16_t*>(wg + (2 * (size_t)i) * l.g);
-    uint16_t* Gl = reinterpret_cast<uint16_t*>(wg + (2 * (size_t)i + 1) * l.g);
-    RowdotOut o{};
+    char* wi = w + (size_t)i * l.per;
+    uint16_t* Gh = reinterpret_cast<uint16_t*>(wi + l.pg);
+    uint16_t* Gl = reinterpret_cast<uint16_t*>(wi + l.pg + l.g);
+    char* w2 = wi + l.pg + 2 * l.g;
+    uint16_t* Gth = reinterpret_cast<uint16_t*>(w2);
+    uint16_t* Gtl = reinterpret_cast<uint16_t*>(w2 + l.planes);
+    uint16_t* XAth = reinterpret_cast<uint16_t*>(w2 + 2 * l.planes);
+    uint16_t* XAtl = reinterpret_cast<uint16_t*>(w2 + 3 * l.planes);
+    Ms[i] = L[i].dY;
+    Vs[i] = L[i].B;
+    Ps[i] = reinterpret_cast<float*>(wi);
+    RowdotOut& o = os[i];
     o.row_hi = Gh;
     o.row_lo = Gl;
     o.scale_row = s;
@@ -308,17 +321,12 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
     o.side = L[i].XA;
     o.side_hi = XAth;
     o.side_lo = XAtl;
-    if (i == 0) {
-      o.zero = counters;  // the batched dX GEMM's split tickets
-      o.nzero = 2 * l.d.nsplit();
-    }
-    e = launch_rowdot(L[i].dY, L[i].B, /*v_lr=*/false, Pg, o, T, N, r, row_chunk(T, N), st);
-    if (e != hipSuccess) return e;
-    TokJob jb{}, ja{};
+    TokJob& jb = tj[2 * i];
+    TokJob& ja = tj[2 * i + 1];
     jb.M = L[i].dY;
     jb.Sh = XAth;
     jb.Sl = XAtl;
-    jb.P = Ptok_b;
+    jb.P = reinterpret_cast<float*>(w2 + 4 * l.planes);
     jb.out = L[i].dB;
     jb.C = N;
     jb.TC = tok_chunk(T, N);
@@ -327,16 +335,22 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
     ja.M = L[i].X;
     ja.Sh = Gth;
     ja.Sl = Gtl;
-    ja.P = Ptok_a;
+    ja.P = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok_b);
     ja.out = L[i].dA;
     ja.C = K;
     ja.TC = tok_chunk(T, K);
     ja.scale = s;
     ja.m_major = 1;
-    e = launch_tokdot2(jb, ja, T, TP, r, st);
-    if (e != hipSuccess) return e;
     p.prob[i] = DxGemmProblem{L[i].dY, L[i].codes, L[i].q8, L[i].s2, L[i].A, Gh, Gl, L[i].dX};
   }
+  os[0].zero = counters;  // the batched dX GEMM's split tickets
+  os[0].nzero = 2 * l.d.nsplit();
+  // G = dY B^T of every problem, then dB and dA of every problem: one launch
+  // of each kernel
+  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/false, Ps, os, T, N, r, row_chunk(T, N), st);
+  if (e != hipSuccess) return e;
+  e = launch_tokdot_n(2 * count, tj, T, TP, r, st);
+  if (e != hipSuccess) return e;
   p.batch = count;
   p.T = T;
   p.K = K;

@@ -60,14 +60,18 @@ __device__ __forceinline__ float4 buf_load_f4(rsrc_t r, uint32_t off) {
 // P[c][t][j] has row stride RP = 64 * JB.
 // ---------------------------------------------------------------------------
 template <bool V_LR, int JB>
-__global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __restrict__ M,
-                                                             const uint16_t* __restrict__ V, float* __restrict__ P,
-                                                             int64_t T, int64_t L, int r, int64_t LC) {
+__global__ __launch_bounds__(256) void rowdot_partial_kernel(RowdotJobs jobs, int64_t T, int64_t L, int r,
+                                                             int64_t LC) {
   __shared__ __align__(16) float red[4][64 * 64];
   constexpr int RP = 64 * JB;
+  // grid.y = jobs x chunks; the job of this workgroup is uniform
+  const int job = __builtin_amdgcn_readfirstlane((int)blockIdx.y / jobs.nc);
+  const uint16_t* __restrict__ M = jobs.M[job];
+  const uint16_t* __restrict__ V = jobs.V[job];
+  float* __restrict__ P = jobs.P[job];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane & 15, g = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const int64_t ch = blockIdx.y;
+  const int64_t ch = (int64_t)blockIdx.y - (int64_t)job * jobs.nc;
   const int64_t lbeg = ch * LC;
   const int64_t lend = lbeg + LC < L ? lbeg + LC : L;
   const int64_t LW = LC / 4;
@@ -185,14 +189,19 @@ __global__ __launch_bounds__(256) void rowdot_partial_kernel(const uint16_t* __r
 // zeros past T) over their whole width TP.
 // ---------------------------------------------------------------------------
 constexpr int kRedRows = 16;
-__global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const float* __restrict__ P, int64_t T,
-                                                            int r, int RP, int nc) {
+__global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOuts outs, RowdotJobs jobs, int64_t T, int r,
+                                                            int RP, int nc) {
   constexpr int kPad = kRedRows + 8;
   __shared__ __align__(16) uint16_t tr[4][64 * kPad];  // [plane][j][t]
+  // grid.y = jobs x j-blocks; the job of this workgroup is uniform
+  const int nj = RP / 64;
+  const int job = __builtin_amdgcn_readfirstlane((int)blockIdx.y / nj);
+  const RowdotOut& o = outs.o[job];
+  const float* __restrict__ P = jobs.P[job];
   const int64_t t0 = (int64_t)blockIdx.x * kRedRows;
-  const int jb = blockIdx.y;
+  const int jb = (int)blockIdx.y - job * nj;
   const bool want_t = o.t_hi != nullptr, want_side = o.side != nullptr;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (blockIdx.x == 0 && jb == 0)
     for (int64_t i = threadIdx.x; i < o.nzero; i += 256) o.zero[i] = 0;
   {
     const int q = threadIdx.x;
@@ -276,14 +285,16 @@ __global__ __launch_bounds__(256) void rowdot_reduce_kernel(RowdotOut o, const f
 // P[c][j][m] has RP rows per chunk.
 // ---------------------------------------------------------------------------
 template <int JT>
-__global__ __launch_bounds__(256) void tokdot_partial_kernel(TokJob j0, TokJob j1, int nwg0, int64_t TP,
-                                                             int64_t T) {
+__global__ __launch_bounds__(256) void tokdot_partial_kernel(TokJobs jobs, int64_t TP, int64_t T) {
   __shared__ __align__(16) float red[4][64 * 64];
   constexpr int RP = 16 * JT;
-  // Workgroups [0, nwg0) serve job 0, the rest job 1 (uniform per workgroup).
-  const bool second = (int)blockIdx.x >= nwg0;
-  const int bid = second ? (int)blockIdx.x - nwg0 : (int)blockIdx.x;
-  const TokJob& jb = second ? j1 : j0;
+  // Workgroups [wg_begin[j], wg_begin[j + 1]) serve job j (uniform).
+  int jsel = 0;
+#pragma unroll
+  for (int j = 1; j < kTokJobsMax; ++j)
+    if (j < jobs.count && (int)blockIdx.x >= jobs.wg_begin[j]) jsel = j;
+  const int bid = (int)blockIdx.x - jobs.wg_begin[jsel];
+  const TokJob& jb = jobs.j[jsel];
   const uint16_t* __restrict__ M = jb.M;
   const uint16_t* __restrict__ Sh = jb.Sh;
   const uint16_t* __restrict__ Sl = jb.Sl;
@@ -391,11 +402,14 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(TokJob j0, TokJob j
 // out = bf16(s * sum over chunks of P[c][j][m]), stored [j][m] (dB: [r,N]) or
 // [m][j] (dA: [K,r]).  Workgroup = a 64 j x 16 m tile; thread q handles 4
 // consecutive m of one j.
-__global__ __launch_bounds__(256) void tokdot_reduce_kernel(TokJob j0, TokJob j1, int nwg0, int r, int RP) {
-  // Workgroups [0, nwg0) serve job 0, the rest job 1 (uniform per workgroup).
-  const bool second = (int)blockIdx.x >= nwg0;
-  const int bid = second ? (int)blockIdx.x - nwg0 : (int)blockIdx.x;
-  const TokJob& job = second ? j1 : j0;
+__global__ __launch_bounds__(256) void tokdot_reduce_kernel(TokJobs jobs, int r, int RP) {
+  // Workgroups [red_begin[j], red_begin[j + 1]) serve job j (uniform).
+  int jsel = 0;
+#pragma unroll
+  for (int j = 1; j < kTokJobsMax; ++j)
+    if (j < jobs.count && (int)blockIdx.x >= jobs.red_begin[j]) jsel = j;
+  const int bid = (int)blockIdx.x - jobs.red_begin[jsel];
+  const TokJob& job = jobs.j[jsel];
   const float* __restrict__ P = job.P;
   uint16_t* __restrict__ out = job.out;
   const int64_t C = job.C;
@@ -452,56 +466,79 @@ __global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* __restrict__ p,
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
-                         int64_t L, int r, int64_t LC, hipStream_t s) {
+hipError_t launch_rowdot_batch(int count, const uint16_t* const* M, const uint16_t* const* V, bool v_lr,
+                               float* const* P, const RowdotOut* o, int64_t T, int64_t L, int r, int64_t LC,
+                               hipStream_t s) {
   const int64_t nc = cdiv(L, LC);
   const int JB = r > 64 ? 2 : 1;
-  dim3 grid((unsigned)cdiv(T, 64), (unsigned)nc);
+  RowdotJobs jobs{};
+  RowdotOuts outs{};
+  jobs.nc = (int)nc;
+  for (int i = 0; i < count; ++i) {
+    jobs.M[i] = M[i];
+    jobs.V[i] = V[i];
+    jobs.P[i] = P[i];
+    outs.o[i] = o[i];
+  }
+  dim3 grid((unsigned)cdiv(T, 64), (unsigned)(nc * count));
   {
     KernelTimer kt_("rowdot_partial_kernel", s);
     if (v_lr) {
-      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<true, 1>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
-      else hipLaunchKernelGGL((rowdot_partial_kernel<true, 2>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<true, 1>), grid, dim3(256), 0, s, jobs, T, L, r, LC);
+      else hipLaunchKernelGGL((rowdot_partial_kernel<true, 2>), grid, dim3(256), 0, s, jobs, T, L, r, LC);
     } else {
-      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<false, 1>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
-      else hipLaunchKernelGGL((rowdot_partial_kernel<false, 2>), grid, dim3(256), 0, s, M, V, P, T, L, r, LC);
+      if (JB == 1) hipLaunchKernelGGL((rowdot_partial_kernel<false, 1>), grid, dim3(256), 0, s, jobs, T, L, r, LC);
+      else hipLaunchKernelGGL((rowdot_partial_kernel<false, 2>), grid, dim3(256), 0, s, jobs, T, L, r, LC);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("rowdot_reduce_kernel", s);
-    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)(cdiv(T, 64) * (64 / kRedRows)), (unsigned)JB), dim3(256),
-                       0, s, o, P, T, r,
-                       64 * JB, (int)nc);
+    hipLaunchKernelGGL(rowdot_reduce_kernel, dim3((unsigned)(cdiv(T, 64) * (64 / kRedRows)), (unsigned)(JB * count)),
+                       dim3(256), 0, s, outs, jobs, T, r, 64 * JB, (int)nc);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s) {
-  TokJob j[2] = {a, b};
-  int nwg[2];
-  for (int i = 0; i < 2; ++i) {
-    j[i].nc = (int)cdiv(T, j[i].TC);
-    j[i].mtiles = (int)cdiv(j[i].C, 64);
-    nwg[i] = j[i].mtiles * j[i].nc;
+hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
+                         int64_t L, int r, int64_t LC, hipStream_t s) {
+  return launch_rowdot_batch(1, &M, &V, v_lr, &P, &o, T, L, r, LC, s);
+}
+
+hipError_t launch_tokdot_n(int count, const TokJob* in, int64_t T, int64_t TP, int r, hipStream_t s) {
+  TokJobs jobs{};
+  jobs.count = count;
+  int nwg = 0, nred = 0;
+  const int jbs = (int)cdiv(r, 64);
+  for (int i = 0; i < count; ++i) {
+    TokJob j = in[i];
+    j.nc = (int)cdiv(T, j.TC);
+    j.mtiles = (int)cdiv(j.C, 64);
+    jobs.j[i] = j;
+    jobs.wg_begin[i] = nwg;
+    jobs.red_begin[i] = nred;
+    nwg += j.mtiles * j.nc;
+    nred += (int)cdiv(j.C, 16) * jbs;
   }
   const int JT = cdiv(r, 16) <= 4 ? 4 : 8;
   {
     KernelTimer kt_("tokdot_partial_kernel", s);
-    const unsigned grid = (unsigned)(nwg[0] + nwg[1]);
-    if (JT == 4) hipLaunchKernelGGL(tokdot_partial_kernel<4>, dim3(grid), dim3(256), 0, s, j[0], j[1], nwg[0], TP, T);
-    else hipLaunchKernelGGL(tokdot_partial_kernel<8>, dim3(grid), dim3(256), 0, s, j[0], j[1], nwg[0], TP, T);
+    if (JT == 4) hipLaunchKernelGGL(tokdot_partial_kernel<4>, dim3((unsigned)nwg), dim3(256), 0, s, jobs, TP, T);
+    else hipLaunchKernelGGL(tokdot_partial_kernel<8>, dim3((unsigned)nwg), dim3(256), 0, s, jobs, TP, T);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("tokdot_reduce_kernel", s);
-    const int jbs = (int)cdiv(r, 64);
-    const int r0 = (int)cdiv(j[0].C, 16) * jbs, r1 = (int)cdiv(j[1].C, 16) * jbs;
-    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)(r0 + r1)), dim3(256), 0, s, j[0], j[1], r0, r, 16 * JT);
+    hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)nred), dim3(256), 0, s, jobs, r, 16 * JT);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s) {
+  const TokJob j[2] = {a, b};
+  return launch_tokdot_n(2, j, T, TP, r, s);
 }
 
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t s) {

@@ -29,8 +29,24 @@ struct RowdotOut {
   int64_t nzero;
 };
 
+// Up to kRowdotJobsMax same-shape rowdots in one launch each of the partial
+// and the reduction kernels.
+constexpr int kRowdotJobsMax = 4;
+struct RowdotJobs {
+  const uint16_t* M[kRowdotJobsMax];
+  const uint16_t* V[kRowdotJobsMax];
+  float* P[kRowdotJobsMax];
+  int nc;  // chunks of the contraction per job
+};
+struct RowdotOuts {
+  RowdotOut o[kRowdotJobsMax];
+};
+
 // out[T][r] = M[T,L] V  with V = A[L,r] (v_lr) or B[r,L]^T.  P is scratch of
 // ceil(L/LC) * T * RP floats; LC a multiple of 128.
+hipError_t launch_rowdot_batch(int count, const uint16_t* const* M, const uint16_t* const* V, bool v_lr,
+                               float* const* P, const RowdotOut* o, int64_t T, int64_t L, int r, int64_t LC,
+                               hipStream_t s);
 hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float* P, const RowdotOut& o, int64_t T,
                          int64_t L, int r, int64_t LC, hipStream_t s);
 
@@ -50,8 +66,17 @@ struct TokJob {
   int nc, mtiles;
 };
 
-// Two tokdots over the same T tokens and rank r in one launch of the partial
-// kernel and one of the reduction (their grids concatenated).
+// Up to kTokJobsMax tokdots over the same T tokens and rank r in one launch
+// of the partial kernel and one of the reduction (their grids concatenated;
+// wg_begin / red_begin are filled by the launcher).
+constexpr int kTokJobsMax = 8;
+struct TokJobs {
+  TokJob j[kTokJobsMax];
+  int wg_begin[kTokJobsMax];
+  int red_begin[kTokJobsMax];
+  int count;
+};
+hipError_t launch_tokdot_n(int count, const TokJob* jobs, int64_t T, int64_t TP, int r, hipStream_t s);
 hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s);
 
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t s);
