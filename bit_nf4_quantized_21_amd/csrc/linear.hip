@@ -32,42 +32,52 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 int64_t rpad(int32_t r) { return round_up(r, 64); }
 
-// Chunk of the contraction of a rowdot (X A or dY B^T): about 256
-// workgroups of 64 rows each, chunks a multiple of 128 long.
-int64_t row_chunk(int64_t T, int64_t L) {
-  const int64_t tiles = cdiv(T, 64);
-  int64_t nc = cdiv(256, tiles);
+// Workgroups a rank-r launch aims for across all its jobs: one per CU.
+constexpr int64_t kRankWGs = 256;
+
+// Chunk of the contraction of a rowdot (X A or dY B^T) of `jobs` same-shape
+// problems in one launch: about kRankWGs workgroups of 64 rows each, chunks
+// a multiple of 128 long.
+int64_t row_chunk(int64_t T, int64_t L, int jobs = 1) {
+  const int64_t tiles = cdiv(T, 64) * jobs;
+  int64_t nc = cdiv(kRankWGs, tiles);
   const int64_t maxc = cdiv(L, 128);
   if (nc > maxc) nc = maxc;
   if (nc < 1) nc = 1;
   return round_up(cdiv(L, nc), 128);
 }
 
-// Token chunk of a tokdot (X^T G or dY^T XA): about 256 workgroups of 64
-// columns each, chunks a multiple of 128 tokens.
-int64_t tok_chunk(int64_t T, int64_t C) {
-  const int64_t tiles = cdiv(C, 64);
-  int64_t nc = cdiv(256, tiles);
+// Token chunk of the tokdots (X^T G, dY^T XA) of one launch, whose jobs
+// have `tiles` 64-column tiles in all: about kRankWGs workgroups, chunks a
+// multiple of 128 tokens.
+int64_t tok_chunk(int64_t T, int64_t tiles) {
+  int64_t nc = cdiv(kRankWGs, tiles);
   const int64_t maxc = cdiv(T, 128);
   if (nc > maxc) nc = maxc;
   if (nc < 1) nc = 1;
   return round_up(cdiv(T, nc), 128);
 }
 
+// The tokdot chunk of the backward of `count` problems of shape K x N.
+int64_t bwd_tok_chunk(int64_t T, int64_t K, int64_t N, int count) {
+  return tok_chunk(T, count * (cdiv(K, 64) + cdiv(N, 64)));
+}
+
 // Backward workspace regions, each 256-byte aligned.
 struct BwdLayout {
   size_t pg, g, planes, ptok_b, ptok_a, slots, counters, xa, pxa, total;
 };
-BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r) {
+// `count` > 1: the per-problem regions of a batch of that many problems.
+BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count = 1) {
   BwdLayout l{};
   const int64_t RP = rpad(r), TP = round_up(T, 64);
-  l.pg = align256((size_t)cdiv(N, row_chunk(T, N)) * T * RP * sizeof(float));
+  l.pg = align256((size_t)cdiv(N, row_chunk(T, N, count)) * T * RP * sizeof(float));
   l.g = align256((size_t)T * RP * sizeof(uint16_t));
   l.planes = align256((size_t)RP * TP * sizeof(uint16_t));
-  const size_t pdb = (size_t)cdiv(T, tok_chunk(T, N)) * RP * N * sizeof(float);
-  const size_t pda = (size_t)cdiv(T, tok_chunk(T, K)) * RP * K * sizeof(float);
-  l.ptok_b = align256(pdb);
-  l.ptok_a = align256(pda);
+  // a tokdot of one chunk writes its output directly and needs no partials
+  const int64_t ntc = cdiv(T, bwd_tok_chunk(T, K, N, count));
+  l.ptok_b = ntc > 1 ? align256((size_t)ntc * RP * N * sizeof(float)) : 0;
+  l.ptok_a = ntc > 1 ? align256((size_t)ntc * RP * K * sizeof(float)) : 0;
   const SplitPlan dp = dx_plan(T, K, N);
   l.slots = dp.S > 1 ? align256((size_t)dp.nsplit() * dp.S * kSplitSlotFloats * sizeof(float)) : 0;
   l.counters = align256((size_t)(dp.nsplit() > 0 ? 2 * dp.nsplit() : 1) * sizeof(int));
@@ -187,7 +197,7 @@ struct FwdBatchLayout {
 };
 FwdBatchLayout fwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
   FwdBatchLayout l{};
-  l.p = align256((size_t)cdiv(K, row_chunk(T, K)) * T * rpad(r) * sizeof(float));
+  l.p = align256((size_t)cdiv(K, row_chunk(T, K, count)) * T * rpad(r) * sizeof(float));
   l.xah = align256((size_t)T * rpad(r) * sizeof(uint16_t));
   l.g = fwd_plan(T, K, N, count);
   l.slots = l.g.S > 1 ? align256((size_t)l.g.nsplit() * l.g.S * kSplitSlotFloats * sizeof(float)) : 0;
@@ -202,7 +212,7 @@ struct BwdBatchLayout {
 };
 BwdBatchLayout bwd_batch_layout(int64_t T, int64_t K, int64_t N, int32_t r, int count) {
   BwdBatchLayout l{};
-  const BwdLayout b = bwd_layout(T, K, N, r);
+  const BwdLayout b = bwd_layout(T, K, N, r, count);
   l.pg = b.pg;
   l.g = b.g;
   l.planes = b.planes;
@@ -259,7 +269,7 @@ hipError_t launch_linear_fwd_batch(int count, const GroupedLinear* L, int64_t T,
   }
   os[0].zero = counters;  // the batched GEMM's split tickets
   os[0].nzero = 2 * l.g.nsplit();
-  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/true, Ps, os, T, K, r, row_chunk(T, K), st);
+  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/true, Ps, os, T, K, r, row_chunk(T, K, count), st);
   if (e != hipSuccess) return e;
   p.batch = count;
   p.T = T;
@@ -329,7 +339,7 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
     jb.P = reinterpret_cast<float*>(w2 + 4 * l.planes);
     jb.out = L[i].dB;
     jb.C = N;
-    jb.TC = tok_chunk(T, N);
+    jb.TC = bwd_tok_chunk(T, K, N, count);
     jb.scale = s;
     jb.m_major = 0;
     ja.M = L[i].X;
@@ -338,7 +348,7 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
     ja.P = reinterpret_cast<float*>(w2 + 4 * l.planes + l.ptok_b);
     ja.out = L[i].dA;
     ja.C = K;
-    ja.TC = tok_chunk(T, K);
+    ja.TC = bwd_tok_chunk(T, K, N, count);
     ja.scale = s;
     ja.m_major = 1;
     p.prob[i] = DxGemmProblem{L[i].dY, L[i].codes, L[i].q8, L[i].s2, L[i].A, Gh, Gl, L[i].dX};
@@ -347,7 +357,7 @@ hipError_t launch_linear_bwd_batch(int count, const GroupedLinearBwd* L, int64_t
   os[0].nzero = 2 * l.d.nsplit();
   // G = dY B^T of every problem, then dB and dA of every problem: one launch
   // of each kernel
-  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/false, Ps, os, T, N, r, row_chunk(T, N), st);
+  e = launch_rowdot_batch(count, Ms, Vs, /*v_lr=*/false, Ps, os, T, N, r, row_chunk(T, N, count), st);
   if (e != hipSuccess) return e;
   e = launch_tokdot_n(2 * count, tj, T, TP, r, st);
   if (e != hipSuccess) return e;
@@ -506,7 +516,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   jb.P = Ptok_b;
   jb.out = dB;
   jb.C = a.N;
-  jb.TC = tok_chunk(a.T, a.N);
+  jb.TC = bwd_tok_chunk(a.T, a.K, a.N, 1);
   jb.scale = a.s;
   jb.m_major = 0;
   ja.M = X;
@@ -515,7 +525,7 @@ hipError_t launch_linear_bwd(const LinearArgs& a, const Codebook& cb, const uint
   ja.P = Ptok_a;
   ja.out = dA;
   ja.C = a.K;
-  ja.TC = tok_chunk(a.T, a.K);
+  ja.TC = bwd_tok_chunk(a.T, a.K, a.N, 1);
   ja.scale = a.s;
   ja.m_major = 1;
   e = launch_tokdot2(jb, ja, a.T, TP, a.r, s);

@@ -371,30 +371,68 @@ __global__ __launch_bounds__(256) void tokdot_partial_kernel(TokJobs jobs, int64
   }
 
   // D[j][m]: lane holds rows j = 16 jt + 4g + i, column m = m0 + 4p + c.
+  // A job whose tokens form one chunk writes its output here (bf16 of
+  // scale x sum, the value the reduction would give); otherwise the
+  // chunk's fp32 tile goes to P.
+  const bool direct = jb.nc == 1;
+  const bool m_major = jb.m_major != 0;
+  uint16_t* __restrict__ out = jb.out;
+  const float sc = jb.scale;
+  const int r = jobs.r;
 #pragma unroll
-  for (int jb = 0; jb < RP / 64 + (RP % 64 ? 1 : 0); ++jb) {
-    if (jb) __syncthreads();
+  for (int ib = 0; ib < RP / 64 + (RP % 64 ? 1 : 0); ++ib) {
+    if (ib) __syncthreads();
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-      if (4 * jb + jt >= JT) break;
+      if (4 * ib + jt >= JT) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * jt + 4 * g + i;
-        const f32x4* a = acc[4 * jb + jt];
+        const f32x4* a = acc[4 * ib + jt];
         *reinterpret_cast<float4*>(&red[wave][j * 64 + 4 * p]) = make_float4(a[0][i], a[1][i], a[2][i], a[3][i]);
       }
     }
     __syncthreads();
-    const int rows = RP - 64 * jb < 64 ? RP - 64 * jb : 64;
+    const int rows = RP - 64 * ib < 64 ? RP - 64 * ib : 64;
+    uint2 packed[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int q = threadIdx.x + 256 * k;
       const int j = q >> 4, m4 = q & 15;
-      if (j >= rows || m0 + 4 * m4 >= C) continue;
       float4 sum = *reinterpret_cast<const float4*>(&red[0][j * 64 + 4 * m4]);
 #pragma unroll
       for (int w = 1; w < 4; ++w) sum = add4(sum, *reinterpret_cast<const float4*>(&red[w][j * 64 + 4 * m4]));
-      *reinterpret_cast<float4*>(P + (ch * RP + 64 * jb + j) * C + m0 + 4 * m4) = sum;
+      packed[k] = make_uint2(pack_bf16x2(sum.x * sc, sum.y * sc), pack_bf16x2(sum.z * sc, sum.w * sc));
+      if (j >= rows || m0 + 4 * m4 >= C) continue;
+      if (!direct) {
+        *reinterpret_cast<float4*>(P + (ch * RP + 64 * ib + j) * C + m0 + 4 * m4) = sum;
+      } else if (!m_major && 64 * ib + j < r) {
+        *reinterpret_cast<uint2*>(out + (64 * ib + j) * C + m0 + 4 * m4) = packed[k];
+      }
+    }
+    if (direct && m_major) {  // uniform per workgroup
+      // Transpose the 64 j x 64 m bf16 tile through LDS so that each
+      // thread stores 8 consecutive j of one row m of out [C][r].
+      uint16_t* tr = reinterpret_cast<uint16_t*>(&red[0][0]);  // [m][j], j padded to 72
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = threadIdx.x + 256 * k;
+        const int j = q >> 4, m4 = q & 15;
+        tr[(4 * m4 + 0) * 72 + j] = (uint16_t)(packed[k].x & 0xFFFFu);
+        tr[(4 * m4 + 1) * 72 + j] = (uint16_t)(packed[k].x >> 16);
+        tr[(4 * m4 + 2) * 72 + j] = (uint16_t)(packed[k].y & 0xFFFFu);
+        tr[(4 * m4 + 3) * 72 + j] = (uint16_t)(packed[k].y >> 16);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int q = threadIdx.x + 256 * k;
+        const int mm = q >> 3, j8 = 8 * (q & 7);
+        if (m0 + mm < C && j8 < rows && 64 * ib + j8 < r)
+          *reinterpret_cast<u32x4*>(out + (m0 + mm) * r + 64 * ib + j8) =
+              *reinterpret_cast<const u32x4*>(&tr[mm * 72 + j8]);
+      }
     }
   }
 }
@@ -519,8 +557,9 @@ hipError_t launch_tokdot_n(int count, const TokJob* in, int64_t T, int64_t TP, i
     jobs.wg_begin[i] = nwg;
     jobs.red_begin[i] = nred;
     nwg += j.mtiles * j.nc;
-    nred += (int)cdiv(j.C, 16) * jbs;
+    if (j.nc > 1) nred += (int)cdiv(j.C, 16) * jbs;  // one chunk: written by the partial kernel
   }
+  jobs.r = r;
   const int JT = cdiv(r, 16) <= 4 ? 4 : 8;
   {
     KernelTimer kt_("tokdot_partial_kernel", s);
@@ -529,6 +568,7 @@ hipError_t launch_tokdot_n(int count, const TokJob* in, int64_t T, int64_t TP, i
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nred == 0) return hipSuccess;
   {
     KernelTimer kt_("tokdot_reduce_kernel", s);
     hipLaunchKernelGGL(tokdot_reduce_kernel, dim3((unsigned)nred), dim3(256), 0, s, jobs, r, 16 * JT);

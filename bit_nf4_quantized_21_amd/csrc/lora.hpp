@@ -75,6 +75,7 @@ struct TokJobs {
   int wg_begin[kTokJobsMax];
   int red_begin[kTokJobsMax];
   int count;
+  int r;
 };
 hipError_t launch_tokdot_n(int count, const TokJob* jobs, int64_t T, int64_t TP, int r, hipStream_t s);
 hipError_t launch_tokdot2(const TokJob& a, const TokJob& b, int64_t T, int64_t TP, int r, hipStream_t s);

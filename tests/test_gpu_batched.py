@@ -2,8 +2,9 @@
 runs of same-shape linears share one dequant-GEMM launch: every linear's Y,
 dX against the oracle (bf16 tolerance) and against its own single call
 (the contraction may be sliced differently, so within tolerance); XA, dA and
-dB bit for bit equal to the single call (same kernels); mixed-shape runs;
-T = 0; and the full-size 65B q/k/v batch on sampled token rows."""
+dB within rounding of the single call (the rank-r contractions are chunked
+for the whole batch); mixed-shape runs; T = 0; and the full-size 65B q/k/v
+batch on sampled token rows."""
 
 import numpy as np
 import pytest
@@ -81,9 +82,13 @@ def test_grouped_gemm_path_against_oracle_and_single(shapes, T, r):
         Y1, XA1 = q.linear_fwd(L["X"], L["codes"], L["q8"], L["s2"], L["A"], L["B"], alpha, L["N"])
         dX1, dA1, dB1 = q.linear_bwd(L["dY"], L["X"], XA1, L["codes"], L["q8"], L["s2"], L["A"], L["B"], alpha)
         torch.cuda.synchronize()
-        assert torch.equal(XA.view(torch.int32), XA1.view(torch.int32))
-        assert torch.equal(dA.view(torch.int16), dA1.view(torch.int16))
-        assert torch.equal(dB.view(torch.int16), dB1.view(torch.int16))
+        # A batch cuts the rank-r contractions into chunks sized for the
+        # whole batch, so its fp32 summation order (and the last bits) may
+        # differ from a single launch's; both are checked against the oracle.
+        xa_scale = float(XA1.abs().max())
+        assert torch.allclose(XA, XA1, rtol=1e-5, atol=1e-6 * xa_scale)
+        _close("dA vs single", _f64(dA), _f64(dA1))
+        _close("dB vs single", _f64(dB), _f64(dB1))
         Yr, dXr, dAr, dBr = _oracle(L, T, r, alpha)
         _close("Y", _f64(Y), Yr)
         _close("dX", _f64(dX), dXr)
