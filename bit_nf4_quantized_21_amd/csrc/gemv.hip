@@ -323,6 +323,16 @@ GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r) {
 }
 
 hipError_t launch_gemv_group(GemvGroup g, const Codebook& cb, hipStream_t s) {
+  // Linears with the longest rows first (a stable sort by K): their
+  // workgroups take the longest, so starting them first keeps the last
+  // round of the grid short.  Each linear keeps its own buffers, so the
+  // order changes no result.
+  for (int a = 1; a < g.count; ++a)
+    for (int b = a; b > 0 && g.L[b].K > g.L[b - 1].K; --b) {
+      const GemvLinear t = g.L[b];
+      g.L[b] = g.L[b - 1];
+      g.L[b - 1] = t;
+    }
   // Row groups per workgroup: the most (4, 2, 1) that still gives at least
   // four workgroups per compute unit over the whole group.
   int RG = 4;
