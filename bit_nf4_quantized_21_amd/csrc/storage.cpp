@@ -212,10 +212,18 @@ int load_4bit(const char* path, const float* const tables[3], int* qtype, int64_
            b.end == b.begin + z.n2 && c.begin == b.end && c.end == c.begin + z.nb;
   }
   if (good) {
+    // The tensors must be exactly the rest of the file; checked before any
+    // buffer is sized from the header, so a forged shape cannot make the
+    // reader allocate more than the file holds.
+    const long pos = std::ftell(f);
+    good = pos > 0 && std::fseek(f, 0, SEEK_END) == 0;
+    const long end = good ? std::ftell(f) : -1;
+    good = good && end >= pos && std::fseek(f, pos, SEEK_SET) == 0 &&
+           (int64_t)(end - pos) == 4 * z.ng + z.n2 + z.nb;
+  }
+  if (good) {
     data.resize((size_t)(4 * z.ng + z.n2 + z.nb));
     good = std::fread(data.data(), 1, data.size(), f) == data.size();
-    char extra;
-    good = good && std::fread(&extra, 1, 1, f) == 0;  // nothing after the tensors
   }
   std::fclose(f);
   if (!good) return kStorageIo;

@@ -211,9 +211,10 @@ int qlora_linear_fwd(const uint16_t* X, int64_t T, int64_t K, int64_t N,
  * (results bit for bit those of qlora_linear_fwd_4bit).  For larger T, every
  * run of up to 4 consecutive linears with the same K and N (q/k/v, gate/up)
  * shares one dequant-GEMM launch over all their output tiles, so small token
- * counts fill the GPU with whole-contraction tiles; results equal
- * qlora_linear_fwd_4bit's within the fp32 accumulation-order tolerance (the
- * contraction may be cut into slices differently).
+ * counts fill the GPU with whole-contraction tiles, and one launch of each
+ * rank-r kernel; results (Y and XA) equal qlora_linear_fwd_4bit's within the
+ * fp32 accumulation-order tolerance (the contractions may be cut into slices
+ * differently, sized for the whole run).
  *   descs    host array of `count` linear descriptors (0 <= count <= 4096);
  *            each names its own X [T,K], weight, A [K,r], B [r,N], and
  *            outputs Y [T,N] and XA [T,r] (device pointers; several linears
@@ -242,8 +243,10 @@ int qlora_linear_fwd_grouped(int32_t qtype, int32_t count, const qlora_linear_de
  * Grouped backward, the counterpart of qlora_linear_fwd_grouped: each linear
  * gets what qlora_linear_bwd_4bit computes for it (dX, dA, dB); runs of up to
  * 4 consecutive linears with the same K and N share one dX dequant-GEMM
- * launch over all their tiles (dX within the accumulation-order tolerance of
- * the single call; dA and dB bit for bit).  T = 0 zeroes every dA and dB.
+ * launch over all their tiles and one launch of each rank-r kernel (dX, dA
+ * and dB within the accumulation-order tolerance of the single call: the
+ * contractions are cut into slices sized for the whole run).  T = 0 zeroes
+ * every dA and dB.
  *   descs  host array of `count` descriptors (0 <= count <= 4096), each with
  *          its own dY [T,N], X [T,K], XA [T,r] (from the forward), weight,
  *          A, B and outputs dX [T,K], dA [K,r], dB [r,N].
