@@ -134,3 +134,31 @@ def test_grouped_65b_qkv_full_size_sampled_rows():
         _close("dX", _f64(dX)[rows], dXr)
         _close("dA", _f64(dA), dAr)
         _close("dB", _f64(dB), dBr)
+
+
+def test_grouped_gemm_path_deterministic():
+    """The batched forward and backward twice on the same inputs (with other
+    work between, so the split hand-offs finish in another order): Y, XA,
+    dX, dA, dB identical bit for bit.  The reductions sum in a fixed order
+    whatever the timing."""
+    q = _q()
+    T, r, alpha = 300, 64, 16.0
+    Ls = _make([(2048, 2048)] * 3 + [(2048, 5632)], T, r, seed0=700)
+
+    def run():
+        fo = q.linear_fwd_grouped(Ls, alpha, T, r)
+        for L, (Y, XA) in zip(Ls, fo):
+            L["XA"] = XA
+        bo = q.linear_bwd_grouped(Ls, alpha, T, r)
+        torch.cuda.synchronize()
+        return [t.clone() for pair in fo for t in pair] + [t.clone() for tri in bo for t in tri]
+
+    a = run()
+    junk = torch.randn(4096, 4096, device="cuda") @ torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    del junk
+    b = run()
+    q.device_status()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
