@@ -67,6 +67,8 @@ def _close(name, got, ref):
     ([(2048, 2048)] * 3, 300, 64),                            # one run of 3 (split tiles)
     ([(520, 640)] * 2 + [(776, 1024)] + [(520, 640)], 257, 16),  # runs 2, 1, 1; ragged
     ([(1024, 4096)] * 4 + [(1024, 4096)], 64, 8),             # a full run of 4, then 1
+    ([(1024, 1024)] * 2, 200, 128),                           # two rank blocks, token chunks
+    ([(1024, 2048)] * 3, 64, 72),                             # rank padded to 128, one token chunk
 ])
 def test_grouped_gemm_path_against_oracle_and_single(shapes, T, r):
     print(f"batched {shapes} T={T} r={r}", flush=True)
