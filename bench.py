@@ -576,6 +576,37 @@ def measure_peaks(torch):
             "probes": "v_mfma_f32_32x32x16_bf16 chains, 4 waves per SIMD; 2 GiB device copy (read + write)"}
 
 
+def dense_gemm_reference(torch, T=512):
+    """Context for the GEMM rate: the same 14 GEMMs of one 65B layer (the
+    forward X W^T and the dX dY W of q, k, v, o, gate, up, down at 512
+    tokens) as dense bf16 torch.matmul (the platform BLAS), with no 4-bit
+    decode and no adapter term; two weight copies per shape, medians of 5
+    event-timed passes."""
+    shapes = [(8192, 8192)] * 4 + [(22016, 8192)] * 2 + [(8192, 22016)]
+    total_us, flops, per = 0.0, 0, {}
+    for (N, K) in sorted(set(shapes)):
+        ws = [torch.randn(N, K, device="cuda", dtype=torch.bfloat16) for _ in range(2)]
+        x = torch.randn(T, K, device="cuda", dtype=torch.bfloat16)
+        dy = torch.randn(T, N, device="cuda", dtype=torch.bfloat16)
+        for w in ws:
+            torch.matmul(x, w.t())
+            torch.matmul(dy, w)
+        fwd = _event_median(torch, lambda i: torch.matmul(x, ws[i % 2].t()), [0, 1], 5)
+        dx = _event_median(torch, lambda i: torch.matmul(dy, ws[i % 2]), [0, 1], 5)
+        n = shapes.count((N, K))
+        total_us += n * (fwd + dx)
+        flops += n * 2 * 2 * T * N * K
+        per[f"{N}x{K}"] = {"fwd_us": round(fwd, 1), "dx_us": round(dx, 1),
+                           "fwd_TFLOPs": round(2 * T * N * K / (fwd * 1e-6) / 1e12, 1),
+                           "dx_TFLOPs": round(2 * T * N * K / (dx * 1e-6) / 1e12, 1)}
+        del ws, x, dy
+        torch.cuda.empty_cache()
+    rate = flops / (total_us * 1e-6) / 1e12
+    return {"workload": "dense bf16 torch.matmul of one 65B layer's forward and dX GEMMs at T=512 "
+                        "(no NF4 decode, no adapter)", "TFLOPs": round(rate, 1),
+            "frac_of_spec": round(rate / PEAK_BF16_TFLOPS, 4), "per_shape": per}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, untouched, on a bounded sample.
 # ---------------------------------------------------------------------------
@@ -729,6 +760,8 @@ def main():
             for leg in ("gemv", "gemv_grouped"):
                 if leg in out:
                     peaks[f"{leg}_frac_of_measured_copy"] = round(out[leg]["value"] / peaks["copy_GBs"], 4)
+        if peaks is not None:
+            peaks["dense_bf16_gemm_reference"] = dense_gemm_reference(torch)
         out["peaks"] = peaks
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
