@@ -191,6 +191,8 @@ hipError_t launch_linear_fwd(const LinearArgs& a, const Codebook& cb, const uint
 // the GPU with whole-contraction tiles instead of contraction slices.
 // ---------------------------------------------------------------------------
 namespace {
+static_assert(kGemmBatchMax <= kRowdotJobsMax && 2 * kGemmBatchMax <= kTokJobsMax,
+              "a batch's rank-r products fit one launch of each kernel");
 struct FwdBatchLayout {
   size_t p, xah, slots, counters, total;
   SplitPlan g;

@@ -507,6 +507,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 hipError_t launch_rowdot_batch(int count, const uint16_t* const* M, const uint16_t* const* V, bool v_lr,
                                float* const* P, const RowdotOut* o, int64_t T, int64_t L, int r, int64_t LC,
                                hipStream_t s) {
+  if (count < 1 || count > kRowdotJobsMax) return hipErrorInvalidValue;
   const int64_t nc = cdiv(L, LC);
   const int JB = r > 64 ? 2 : 1;
   RowdotJobs jobs{};
@@ -545,6 +546,7 @@ hipError_t launch_rowdot(const uint16_t* M, const uint16_t* V, bool v_lr, float*
 }
 
 hipError_t launch_tokdot_n(int count, const TokJob* in, int64_t T, int64_t TP, int r, hipStream_t s) {
+  if (count < 1 || count > kTokJobsMax) return hipErrorInvalidValue;
   TokJobs jobs{};
   jobs.count = count;
   int nwg = 0, nred = 0;
