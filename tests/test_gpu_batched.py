@@ -164,3 +164,40 @@ def test_grouped_gemm_path_deterministic():
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
+def _random_cases(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        count = int(rng.integers(2, 5))
+        N = int(rng.integers(1, 320)) * 8
+        K = int(rng.integers(1, 40)) * 64
+        T = int(rng.integers(17, 700))
+        r = int(rng.choice([8, 16, 24, 64, 72, 120, 128]))
+        cases.append(([(N, K)] * count, T, r))
+    return cases
+
+
+@pytest.mark.parametrize("shapes,T,r", _random_cases(6))
+def test_batched_random_shapes_against_oracle(shapes, T, r):
+    """Seeded random batches (2-4 same-shape linears, N and K up to ~2500,
+    ragged T up to 700, ranks 8-128): every output against the oracle on
+    sampled token rows (Y, dX) and in full (dA, dB)."""
+    print(f"batched random {shapes[0]} x{len(shapes)} T={T} r={r}", flush=True)
+    q = _q()
+    alpha = 16.0
+    Ls = _make(shapes, T, r, seed0=T * 7 + r)
+    fo = q.linear_fwd_grouped(Ls, alpha, T, r)
+    for L, (Y, XA) in zip(Ls, fo):
+        L["XA"] = XA
+    bo = q.linear_bwd_grouped(Ls, alpha, T, r)
+    torch.cuda.synchronize()
+    q.device_status()
+    rows = np.unique(np.array([0, 1, T // 3, T // 2, T - 2, T - 1]))
+    for L, (Y, _), (dX, dA, dB) in zip(Ls, fo, bo):
+        Yr, dXr, dAr, dBr = _oracle(L, T, r, alpha, rows)
+        _close("Y", _f64(Y)[rows], Yr)
+        _close("dX", _f64(dX)[rows], dXr)
+        _close("dA", _f64(dA), dAr)
+        _close("dB", _f64(dB), dBr)
