@@ -59,7 +59,10 @@ __device__ __forceinline__ void load_weights4(const uint16_t* __restrict__ W, in
   }
 }
 
-constexpr int kBins = 128;             // uniform bins of w / absmax over [-1, 1]
+// Uniform bins of w / absmax over [-1, 1]: the host picks a count between
+// kBinsMin and kBinsMax (128 first) whose bins separate the type's
+// boundaries.
+constexpr int kBinsMin = 96, kBinsMax = 160;
 constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
 
 // Exact scan: level = #{j : w > absmax * m_j} over the type's boundaries
@@ -72,7 +75,7 @@ __device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoin
   return a64 == 0.0 ? mp.zero_code : level_code(mp, c);
 }
 
-// Bin tables of a type in LDS: every bin of width 2/kBins holds at most one
+// Bin tables of a type in LDS: every bin of width 2/nbins holds at most one
 // level boundary, none within 1e-5 of a bin edge (checked on the host before
 // the binned kernels are chosen), so the bin of the fp32 estimate
 // x = w * (1/absmax) (error < 1e-6) contains x's true position or is a
@@ -80,12 +83,12 @@ __device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoin
 // (+inf when it has none); code[b] holds the code below it in bits 0..7 and
 // the code above it in bits 8..15.
 struct BinTables {
-  double thr[kBins];
-  uint32_t code[kBins];
+  double thr[kBinsMax];
+  uint32_t code[kBinsMax];
 };
-__device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const Midpoints& mp) {
-  if (threadIdx.x < kBins) {
-    const double lo = -1.0 + threadIdx.x * (2.0 / kBins), hi = lo + 2.0 / kBins;
+__device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const Midpoints& mp, int nbins) {
+  if ((int)threadIdx.x < nbins) {
+    const double lo = -1.0 + threadIdx.x * (2.0 / nbins), hi = lo + 2.0 / nbins;
     uint32_t cnt = 0;
     double thr = __builtin_inf();
 #pragma unroll
@@ -101,24 +104,23 @@ __device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const Midpoints&
 // Quantizes the block held by a 16-lane group (lane l16 holds elements
 // 4 l16 .. 4 l16 + 3 in v): returns the 4 codes packed low nibble first and
 // the block's absmax in *amax (on every lane of the group).
-template <bool BINNED>
 __device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Midpoints& mp, const BinTables& bt,
-                                                   float* amax) {
+                                                   int nbins, float* amax) {
   float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
   for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
   *amax = a;
   const double a64 = (double)a;
   uint32_t c[4];
-  if (!BINNED || a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> the zero code
+  if (a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> the zero code
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = scan_code(v[i], a64, mp);
   } else {
-    const float inv = __builtin_amdgcn_rcpf(a);
+    const float inv = __builtin_amdgcn_rcpf(a), half = 0.5f * (float)nbins;  // half is exact
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int b = (int)((v[i] * inv + 1.0f) * (0.5f * kBins));
-      b = b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b);
+      int b = (int)((v[i] * inv + 1.0f) * half);
+      b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
       const uint32_t cc = bt.code[b];
       c[i] = ((double)v[i] > a64 * bt.thr[b]) ? (cc >> 8) : (cc & 0xFFu);
     }
@@ -136,14 +138,12 @@ __device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, int64_
   }
 }
 
-template <typename T, bool BINNED>
+template <typename T>
 __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
-                                                float* __restrict__ absmax, const Midpoints& mp) {
+                                                float* __restrict__ absmax, const Midpoints& mp, int nbins) {
   __shared__ BinTables bt;
-  if (BINNED) {
-    bin_tables_to_lds(bt, mp);
-    __syncthreads();
-  }
+  bin_tables_to_lds(bt, mp, nbins);
+  __syncthreads();
   const int64_t nb = (n + kBlock - 1) / kBlock;
   constexpr int G = kQGroupBlocks;
   const int64_t blk0 = ((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) * G;
@@ -157,7 +157,7 @@ __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t
     const int64_t blk = blk0 + g;
     if (blk >= nb) break;  // uniform per 16-lane group
     float a;
-    const uint32_t packed = quantize_block<BINNED>(v[g], mp, bt, &a);
+    const uint32_t packed = quantize_block(v[g], mp, bt, nbins, &a);
     if (l16 == 0) absmax[blk] = a;
     store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
   }
@@ -167,24 +167,15 @@ __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t
 // apart.
 __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
                                                            uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                           Midpoints mp) {
-  quantize_blocks<float, true>(W, n, codes, absmax, mp);
+                                                           Midpoints mp, int nbins) {
+  quantize_blocks<float>(W, n, codes, absmax, mp, nbins);
 }
 __global__ __launch_bounds__(256) void quantize_nf4_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
                                                                 uint8_t* __restrict__ codes,
-                                                                float* __restrict__ absmax, Midpoints mp) {
-  quantize_blocks<uint16_t, true>(W, n, codes, absmax, mp);
+                                                                float* __restrict__ absmax, Midpoints mp,
+                                                                int nbins) {
+  quantize_blocks<uint16_t>(W, n, codes, absmax, mp, nbins);
 }
-// Exact linear scan over the boundaries for every weight (types whose
-// boundaries the bins do not separate, e.g. FP4, whose boundary 1/8 lies on
-// a bin edge).
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const T* __restrict__ W, int64_t n,
-                                                                uint8_t* __restrict__ codes,
-                                                                float* __restrict__ absmax, Midpoints mp) {
-  quantize_blocks<T, false>(W, n, codes, absmax, mp);
-}
-
 // ---------------------------------------------------------------------------
 // Fused quantize + double quant: W[n] -> codes[n/2], q8[nb], s2[ceil(nb/256)].
 // One workgroup per group of 256 blocks (16384 weights): four passes of 64
@@ -194,14 +185,14 @@ __global__ __launch_bounds__(256) void quantize_nf4_scan_kernel(const T* __restr
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t q8_code(float c, double s2d, double scale);
 
-template <typename T, bool BINNED>
+template <typename T>
 __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ q8, float* __restrict__ s2,
-                                                  const Midpoints& mp) {
+                                                  const Midpoints& mp, int nbins) {
   __shared__ BinTables bt;
   __shared__ float s_amax[kBlock2];
   __shared__ float s_wmax[4];
-  if (BINNED) bin_tables_to_lds(bt, mp);
+  bin_tables_to_lds(bt, mp, nbins);
   __syncthreads();
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t gblk = (int64_t)blockIdx.x * kBlock2;  // first block of the group
@@ -221,7 +212,7 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
     for (int g = 0; g < G; ++g) {
       const int64_t blk = gblk + local0 + g;
       float a;
-      const uint32_t packed = quantize_block<BINNED>(v[g], mp, bt, &a);  // every lane group takes part
+      const uint32_t packed = quantize_block(v[g], mp, bt, nbins, &a);  // every lane group takes part
       if (l16 == 0) s_amax[local0 + g] = a;                                // 0 past the last block
       if (blk < nb) store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
     }
@@ -245,21 +236,14 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
 
 __global__ __launch_bounds__(256) void quantize_dq_kernel(const float* __restrict__ W, int64_t n,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
-                                                          float* __restrict__ s2, Midpoints mp) {
-  quantize_dq_group<float, true>(W, n, codes, q8, s2, mp);
+                                                          float* __restrict__ s2, Midpoints mp, int nbins) {
+  quantize_dq_group<float>(W, n, codes, q8, s2, mp, nbins);
 }
 __global__ __launch_bounds__(256) void quantize_dq_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ q8, float* __restrict__ s2,
-                                                               Midpoints mp) {
-  quantize_dq_group<uint16_t, true>(W, n, codes, q8, s2, mp);
-}
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_dq_scan_kernel(const T* __restrict__ W, int64_t n,
-                                                               uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ q8, float* __restrict__ s2,
-                                                               Midpoints mp) {
-  quantize_dq_group<T, false>(W, n, codes, q8, s2, mp);
+                                                               Midpoints mp, int nbins) {
+  quantize_dq_group<uint16_t>(W, n, codes, q8, s2, mp, nbins);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,11 +340,11 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------------------
 namespace {
-// The bins can be used when each holds at most one boundary of the type and
-// none lies within 1e-5 of a bin edge.
-bool bins_separate(const Midpoints& mp) {
-  for (int b = 0; b < kBins; ++b) {
-    const double lo = -1.0 + b * (2.0 / kBins), hi = lo + 2.0 / kBins;
+// nbins uniform bins can be used when each holds at most one boundary of the
+// type and none lies within 1e-5 of a bin edge.
+bool bins_separate(const Midpoints& mp, int nbins) {
+  for (int b = 0; b < nbins; ++b) {
+    const double lo = -1.0 + b * (2.0 / nbins), hi = lo + 2.0 / nbins;
     int inside = 0;
     for (int j = 0; j < 15; ++j) {
       if (!std::isfinite(mp.m[j])) continue;
@@ -372,35 +356,46 @@ bool bins_separate(const Midpoints& mp) {
   return true;
 }
 
+// The bin count for a type: 128, else the nearest count in range that
+// separates its boundaries (INT4's and FP4's fall on edges of 128 bins;
+// 127 separates NF4, INT4 and FP4 alike); 0 when none does, and the
+// launchers then refuse the call (no shipped type comes to that).
+int choose_bins(const Midpoints& mp) {
+  for (int d = 0; d <= kBinsMax - kBinsMin; ++d) {
+    const int lo = 128 - d, hi = 128 + d;
+    if (lo >= kBinsMin && bins_separate(mp, lo)) return lo;
+    if (hi <= kBinsMax && bins_separate(mp, hi)) return hi;
+  }
+  return 0;
+}
+
 template <typename T>
-hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints), const T* W,
+hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints, int), const T* W,
                              int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp, const char* name,
                              hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   constexpr int G = kQGroupBlocks;
   const int64_t grid = (nb + 16 * G - 1) / (16 * G);
-  if (bins_separate(mp)) {
+  const int nbins = choose_bins(mp);
+  if (nbins == 0) return hipErrorInvalidValue;
+  {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
-  } else {
-    KernelTimer kt_("quantize_nf4_scan_kernel", s);
-    hipLaunchKernelGGL(quantize_nf4_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp, nbins);
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, uint8_t*, float*, Midpoints),
+hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, uint8_t*, float*, Midpoints, int),
                                 const T* W, int64_t n, uint8_t* codes, uint8_t* q8, float* s2, const Midpoints& mp,
                                 const char* name, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t grid = (nb + kBlock2 - 1) / kBlock2;
-  if (bins_separate(mp)) {
+  const int nbins = choose_bins(mp);
+  if (nbins == 0) return hipErrorInvalidValue;
+  {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp);
-  } else {
-    KernelTimer kt_("quantize_dq_scan_kernel", s);
-    hipLaunchKernelGGL(quantize_dq_scan_kernel<T>, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp, nbins);
   }
   return hipGetLastError();
 }
