@@ -256,3 +256,28 @@ def test_argument_errors_raise():
     B = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(q.QLoRAError):
         q.linear_fwd(X, codes, q8, s2, A, B, 16.0, 64)   # K = 96 is not a multiple of 64
+
+
+def _random_single_cases(n, seed=4242):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.integers(1, 300)) * 8
+        K = int(rng.integers(1, 36)) * 64
+        # half the cases on the small-token path (T <= 16), half above it
+        T = int(rng.integers(1, 17)) if i % 2 == 0 else int(rng.integers(17, 600))
+        r = int(rng.choice([8, 16, 24, 40, 64, 72, 96, 128]))
+        cases.append((N, K, T, r))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,T,r", _random_single_cases(8))
+def test_random_shapes_against_oracle(N, K, T, r):
+    """Seeded random single linears (N up to ~2400, K up to ~2200, T on both
+    sides of the small-token boundary, ranks 8-128): codes and constants bit
+    for bit, Y, XA, dX on sampled rows and dA, dB in full against the
+    oracle."""
+    print(f"random single N={N} K={K} T={T} r={r}", flush=True)
+    c = Case(N, K, T, r, seed=N * 3 + K + T)
+    rows = np.unique(np.array([0, T // 3, T // 2, T - 1]))
+    _check(c, c.gpu(), rows=rows)
