@@ -75,29 +75,23 @@ __device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoin
   return a64 == 0.0 ? mp.zero_code : level_code(mp, c);
 }
 
-// Bin tables of a type in LDS: every bin of width 2/nbins holds at most one
-// level boundary, none within 1e-5 of a bin edge (checked on the host before
-// the binned kernels are chosen), so the bin of the fp32 estimate
-// x = w * (1/absmax) (error < 1e-6) contains x's true position or is a
-// neighbour separated from it by no boundary.  thr[b] is the bin's boundary
-// (+inf when it has none); code[b] holds the code below it in bits 0..7 and
-// the code above it in bits 8..15.
+// Bin tables of a type: every bin of width 2/nbins holds at most one level
+// boundary, none within 1e-5 of a bin edge (checked on the host before the
+// tables are built), so the bin of the fp32 estimate x = w * (1/absmax)
+// (error < 1e-6) contains x's true position or is a neighbour separated from
+// it by no boundary.  thr[b] is the bin's boundary (+inf when it has none);
+// code[b] holds the code below it in bits 0..7 and the code above it in bits
+// 8..15.  The host builds them once per launch and passes them by value; each
+// workgroup copies them into LDS.
 struct BinTables {
   double thr[kBinsMax];
   uint32_t code[kBinsMax];
+  int nbins;
 };
-__device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const Midpoints& mp, int nbins) {
-  if ((int)threadIdx.x < nbins) {
-    const double lo = -1.0 + threadIdx.x * (2.0 / nbins), hi = lo + 2.0 / nbins;
-    uint32_t cnt = 0;
-    double thr = __builtin_inf();
-#pragma unroll
-    for (int j = 0; j < 15; ++j) {
-      if (mp.m[j] < lo) cnt += 1;
-      else if (mp.m[j] < hi) thr = mp.m[j];
-    }
-    t.thr[threadIdx.x] = thr;
-    t.code[threadIdx.x] = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 8);
+__device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const BinTables& src) {
+  if ((int)threadIdx.x < src.nbins) {
+    t.thr[threadIdx.x] = src.thr[threadIdx.x];
+    t.code[threadIdx.x] = src.code[threadIdx.x];
   }
 }
 
@@ -140,9 +134,11 @@ __device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, int64_
 
 template <typename T>
 __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
-                                                float* __restrict__ absmax, const Midpoints& mp, int nbins) {
+                                                float* __restrict__ absmax, const Midpoints& mp,
+                                                const BinTables& bins) {
   __shared__ BinTables bt;
-  bin_tables_to_lds(bt, mp, nbins);
+  const int nbins = bins.nbins;
+  bin_tables_to_lds(bt, bins);
   __syncthreads();
   const int64_t nb = (n + kBlock - 1) / kBlock;
   constexpr int G = kQGroupBlocks;
@@ -167,14 +163,14 @@ __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t
 // apart.
 __global__ __launch_bounds__(256) void quantize_nf4_kernel(const float* __restrict__ W, int64_t n,
                                                            uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                           Midpoints mp, int nbins) {
-  quantize_blocks<float>(W, n, codes, absmax, mp, nbins);
+                                                           Midpoints mp, BinTables bins) {
+  quantize_blocks<float>(W, n, codes, absmax, mp, bins);
 }
 __global__ __launch_bounds__(256) void quantize_nf4_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ absmax, Midpoints mp,
-                                                                int nbins) {
-  quantize_blocks<uint16_t>(W, n, codes, absmax, mp, nbins);
+                                                                BinTables bins) {
+  quantize_blocks<uint16_t>(W, n, codes, absmax, mp, bins);
 }
 // ---------------------------------------------------------------------------
 // Fused quantize + double quant: W[n] -> codes[n/2], q8[nb], s2[ceil(nb/256)].
@@ -188,11 +184,12 @@ __device__ __forceinline__ uint32_t q8_code(float c, double s2d, double scale);
 template <typename T>
 __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64_t n, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ q8, float* __restrict__ s2,
-                                                  const Midpoints& mp, int nbins) {
+                                                  const Midpoints& mp, const BinTables& bins) {
   __shared__ BinTables bt;
   __shared__ float s_amax[kBlock2];
   __shared__ float s_wmax[4];
-  bin_tables_to_lds(bt, mp, nbins);
+  const int nbins = bins.nbins;
+  bin_tables_to_lds(bt, bins);
   __syncthreads();
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t gblk = (int64_t)blockIdx.x * kBlock2;  // first block of the group
@@ -236,14 +233,14 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
 
 __global__ __launch_bounds__(256) void quantize_dq_kernel(const float* __restrict__ W, int64_t n,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
-                                                          float* __restrict__ s2, Midpoints mp, int nbins) {
-  quantize_dq_group<float>(W, n, codes, q8, s2, mp, nbins);
+                                                          float* __restrict__ s2, Midpoints mp, BinTables bins) {
+  quantize_dq_group<float>(W, n, codes, q8, s2, mp, bins);
 }
 __global__ __launch_bounds__(256) void quantize_dq_bf16_kernel(const uint16_t* __restrict__ W, int64_t n,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ q8, float* __restrict__ s2,
-                                                               Midpoints mp, int nbins) {
-  quantize_dq_group<uint16_t>(W, n, codes, q8, s2, mp, nbins);
+                                                               Midpoints mp, BinTables bins) {
+  quantize_dq_group<uint16_t>(W, n, codes, q8, s2, mp, bins);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,8 +366,27 @@ int choose_bins(const Midpoints& mp) {
   return 0;
 }
 
+// The tables of nbins bins (the rule is stated at BinTables).
+BinTables make_bins(const Midpoints& mp, int nbins) {
+  BinTables t{};
+  t.nbins = nbins;
+  for (int b = 0; b < nbins; ++b) {
+    const double lo = -1.0 + b * (2.0 / nbins), hi = lo + 2.0 / nbins;
+    uint32_t cnt = 0;
+    double thr = HUGE_VAL;
+    for (int j = 0; j < 15; ++j) {
+      if (mp.m[j] < lo) cnt += 1;
+      else if (mp.m[j] < hi) thr = mp.m[j];
+    }
+    t.thr[b] = thr;
+    t.code[b] = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 8);
+  }
+  return t;
+}
+
 template <typename T>
-hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints, int), const T* W,
+hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, float*, Midpoints, BinTables),
+                             const T* W,
                              int64_t n, uint8_t* codes, float* absmax, const Midpoints& mp, const char* name,
                              hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
@@ -380,13 +396,15 @@ hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, 
   if (nbins == 0) return hipErrorInvalidValue;
   {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp, nbins);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp,
+                       make_bins(mp, nbins));
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, uint8_t*, float*, Midpoints, int),
+hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, uint8_t*, float*, Midpoints,
+                                                      BinTables),
                                 const T* W, int64_t n, uint8_t* codes, uint8_t* q8, float* s2, const Midpoints& mp,
                                 const char* name, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
@@ -395,7 +413,8 @@ hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t
   if (nbins == 0) return hipErrorInvalidValue;
   {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp, nbins);
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp,
+                       make_bins(mp, nbins));
   }
   return hipGetLastError();
 }
