@@ -95,14 +95,24 @@ __device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const BinTables&
   }
 }
 
+// Maximum over the 16 lanes of a DPP row, on every lane of the row: swaps
+// within quads (quad_perm [1,0,3,2], then [2,3,0,1]), then the half-row and
+// the row mirrors.  VALU only (a cross-lane shuffle would go through the LDS
+// crossbar); the maximum of the same 16 values, so the same bits.
+__device__ __forceinline__ float row16_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, false)));
+  return a;
+}
+
 // Quantizes the block held by a 16-lane group (lane l16 holds elements
 // 4 l16 .. 4 l16 + 3 in v): returns the 4 codes packed low nibble first and
 // the block's absmax in *amax (on every lane of the group).
 __device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Midpoints& mp, const BinTables& bt,
                                                    int nbins, float* amax) {
-  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-  for (int off = 8; off; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+  const float a = row16_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
   *amax = a;
   const double a64 = (double)a;
   uint32_t c[4];
