@@ -17,6 +17,8 @@
 // the fused quantizer gives each group of 256 blocks to one workgroup and
 // keeps the absmax values on chip.
 #include <cmath>
+#include <cstdint>
+#include <type_traits>
 
 #include "common.hpp"
 #include "timing.hpp"
@@ -156,6 +158,20 @@ __device__ __forceinline__ void quantize_blocks(const T* __restrict__ W, int64_t
   const int l16 = threadIdx.x & 15;
   if (blk0 >= nb) return;  // whole 16-lane groups leave together (after the barrier)
   float v[G][4];
+  if ((blk0 + G) * kBlock <= n) {
+    // Every block of the group is whole (all but the last groups): plain
+    // vector loads and stores, no per-element range checks.
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_weights4(W, INT64_MAX, (blk0 + g) * kBlock + l16 * 4, v[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a;
+      const uint32_t packed = quantize_block(v[g], mp, bt, nbins, &a);
+      if (l16 == 0) absmax[blk0 + g] = a;
+      store_codes4(codes, INT64_MAX, (blk0 + g) * kBlock + l16 * 4, packed);
+    }
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) load_weights4(W, n, (blk0 + g) * kBlock + l16 * 4, v[g]);
 #pragma unroll
@@ -205,25 +221,35 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
   const int64_t gblk = (int64_t)blockIdx.x * kBlock2;  // first block of the group
   const int l16 = threadIdx.x & 15, lg = threadIdx.x >> 4;
   constexpr int G = kQGroupBlocks;
+  // The four passes of 64 blocks; FULL: all 256 blocks of the group are
+  // whole (every group but the last), so loads and stores need no range
+  // checks.
+  auto passes = [&](auto full) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-  for (int pass = 0; pass < kBlock2 / (16 * G); ++pass) {
-    const int local0 = pass * 16 * G + lg * G;  // block of the group, 0..255
-    float v[G][4];
+    for (int pass = 0; pass < kBlock2 / (16 * G); ++pass) {
+      const int local0 = pass * 16 * G + lg * G;  // block of the group, 0..255
+      float v[G][4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t blk = gblk + local0 + g;
-      if (blk < nb) load_weights4(W, n, blk * kBlock + l16 * 4, v[g]);
-      else v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.0f;
+      for (int g = 0; g < G; ++g) {
+        const int64_t blk = gblk + local0 + g;
+        if (FULL) load_weights4(W, INT64_MAX, blk * kBlock + l16 * 4, v[g]);
+        else if (blk < nb) load_weights4(W, n, blk * kBlock + l16 * 4, v[g]);
+        else v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t blk = gblk + local0 + g;
+        float a;
+        const uint32_t packed = quantize_block(v[g], mp, bt, nbins, &a);  // every lane group takes part
+        if (l16 == 0) s_amax[local0 + g] = a;                                // 0 past the last block
+        if (FULL) store_codes4(codes, INT64_MAX, blk * kBlock + l16 * 4, packed);
+        else if (blk < nb) store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
+      }
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t blk = gblk + local0 + g;
-      float a;
-      const uint32_t packed = quantize_block(v[g], mp, bt, nbins, &a);  // every lane group takes part
-      if (l16 == 0) s_amax[local0 + g] = a;                                // 0 past the last block
-      if (blk < nb) store_codes4(codes, n, blk * kBlock + l16 * 4, packed);
-    }
-  }
+  };
+  if ((gblk + kBlock2) * kBlock <= n) passes(std::true_type{});  // uniform over the workgroup
+  else passes(std::false_type{});
   __syncthreads();
   // s2 = the group's maximum absmax (exact fp32; the zeros past the last
   // block never raise it), then q8 of block t.
