@@ -79,33 +79,40 @@ __device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoin
 
 // Bin tables of a type: every bin of width 2/nbins holds at most one level
 // boundary, none within 1e-5 of a bin edge (checked on the host before the
-// tables are built), so the bin of the fp32 estimate x = w * (1/absmax)
-// (error < 1e-6) contains x's true position or is a neighbour separated from
-// it by no boundary.  thr[b] is the bin's boundary (+inf when it has none);
-// code[b] holds the code below it in bits 0..7 and the code above it in bits
-// 8..15.  The host builds them once per launch and passes them by value; each
-// workgroup copies them into LDS.
+// tables are built), so the bin of the fp32 estimate of w / absmax (error
+// below 1e-6) contains its true position or is a neighbour separated from it
+// by no boundary.  Entry b: thr, the bin's boundary (+inf when it has none),
+// and code, the code below it in bits 0..3 and the code above it in bits
+// 4..7; 16 bytes, so one address reaches both.  The host builds them once per
+// launch and passes them by value; each workgroup copies them into LDS.
+struct BinEntry {
+  double thr;
+  uint32_t code, pad;
+};
 struct BinTables {
-  double thr[kBinsMax];
-  uint32_t code[kBinsMax];
+  BinEntry e[kBinsMax];
   int nbins;
 };
 __device__ __forceinline__ void bin_tables_to_lds(BinTables& t, const BinTables& src) {
-  if ((int)threadIdx.x < src.nbins) {
-    t.thr[threadIdx.x] = src.thr[threadIdx.x];
-    t.code[threadIdx.x] = src.code[threadIdx.x];
-  }
+  if ((int)threadIdx.x < src.nbins) t.e[threadIdx.x] = src.e[threadIdx.x];
 }
+
+// a = max(a, a of the lane that the DPP control names), within rows of 16
+// lanes.  One v_max_f32 with a DPP source (the builtin form adds a NaN
+// canonicalization per step); s_nop 1 covers the wait states between a VALU
+// write of a and its DPP read.
+#define QLORA_ROW_MAX_STEP(a, ctrl) \
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf" : "=v"(a) : "v"(a))
 
 // Maximum over the 16 lanes of a DPP row, on every lane of the row: swaps
 // within quads (quad_perm [1,0,3,2], then [2,3,0,1]), then the half-row and
 // the row mirrors.  VALU only (a cross-lane shuffle would go through the LDS
 // crossbar); the maximum of the same 16 values, so the same bits.
 __device__ __forceinline__ float row16_max(float a) {
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false)));
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false)));
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, false)));
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, false)));
+  QLORA_ROW_MAX_STEP(a, "quad_perm:[1,0,3,2]");
+  QLORA_ROW_MAX_STEP(a, "quad_perm:[2,3,0,1]");
+  QLORA_ROW_MAX_STEP(a, "row_half_mirror");
+  QLORA_ROW_MAX_STEP(a, "row_mirror");
   return a;
 }
 
@@ -122,13 +129,16 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Mi
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = scan_code(v[i], a64, mp);
   } else {
-    const float inv = __builtin_amdgcn_rcpf(a), half = 0.5f * (float)nbins;  // half is exact
+    // Bin position x = (w / absmax + 1) nbins / 2 as one fma; x > -1 since
+    // |w| <= absmax, so truncation never goes below bin 0, and w = absmax
+    // reaches x = nbins, the last bin's upper edge.
+    const float half = 0.5f * (float)nbins, ih = __builtin_amdgcn_rcpf(a) * half;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int b = (int)((v[i] * inv + 1.0f) * half);
-      b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
-      const uint32_t cc = bt.code[b];
-      c[i] = ((double)v[i] > a64 * bt.thr[b]) ? (cc >> 8) : (cc & 0xFFu);
+      int b = (int)__builtin_fmaf(v[i], ih, half);
+      b = b < nbins - 1 ? b : nbins - 1;
+      const BinEntry& e = bt.e[b];
+      c[i] = (e.code >> (((double)v[i] > a64 * e.thr) ? 4 : 0)) & 15u;
     }
   }
   return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
@@ -414,8 +424,9 @@ BinTables make_bins(const Midpoints& mp, int nbins) {
       if (mp.m[j] < lo) cnt += 1;
       else if (mp.m[j] < hi) thr = mp.m[j];
     }
-    t.thr[b] = thr;
-    t.code[b] = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 8);
+    t.e[b].thr = thr;
+    t.e[b].code = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 4);
+    t.e[b].pad = 0;
   }
   return t;
 }
