@@ -236,10 +236,9 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
   // checks.
   auto passes = [&](auto full) {
     constexpr bool FULL = decltype(full)::value;
-#pragma unroll
-    for (int pass = 0; pass < kBlock2 / (16 * G); ++pass) {
-      const int local0 = pass * 16 * G + lg * G;  // block of the group, 0..255
-      float v[G][4];
+    constexpr int kPasses = kBlock2 / (16 * G);
+    auto load_pass = [&](int pass, float (&v)[G][4]) {
+      const int local0 = pass * 16 * G + lg * G;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int64_t blk = gblk + local0 + g;
@@ -247,6 +246,15 @@ __device__ __forceinline__ void quantize_dq_group(const T* __restrict__ W, int64
         else if (blk < nb) load_weights4(W, n, blk * kBlock + l16 * 4, v[g]);
         else v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.0f;
       }
+    };
+    // The next pass's weights are loading while this pass is decided.
+    float vb[2][G][4];
+    load_pass(0, vb[0]);
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int local0 = pass * 16 * G + lg * G;  // block of the group, 0..255
+      if (pass + 1 < kPasses) load_pass(pass + 1, vb[(pass + 1) & 1]);
+      float (&v)[G][4] = vb[pass & 1];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int64_t blk = gblk + local0 + g;
