@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
 
   codebook_to_lds(lut16, cb, tid);
 
-  const int wave = tid >> 6, lane = tid & 63, ml = lane & 31, h = lane >> 5;
+  // wave is uniform: readfirstlane lets the compiler keep what derives from it
+  // (LDS addresses of the buffer-to-LDS copies, M0) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, ml = lane & 31, h = lane >> 5;
   const int64_t T = p.T, K = p.K, N = p.N;
   const int64_t n0 = (int64_t)tn * kTileN, m0 = (int64_t)tm * kTileM;
   const int64_t K2 = K / 2, bpr = K / 64;
