@@ -65,9 +65,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   unsigned char* const xring[4] = {xs0, xs1, xs2, xs3};
   const int tid = threadIdx.x;
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; tiles are ordered
-  // token-tile-major and each XCD takes a contiguous run of them, so the X
-  // tile (the operand re-read by every n-tile) stays in that XCD's L2.
+  // Workgroups are dispatched round-robin over the 8 XCDs and each XCD takes
+  // a contiguous run of tiles.  With many token tiles the tiles are ordered
+  // token-tile-major, so an X tile (re-read by every n-tile) stays in that
+  // XCD's L2; with at most two (T <= 512) they are ordered n-tile-major, so
+  // the tiles that share an n-tile's codes run together (measured 2.5 %
+  // faster at T = 512).
   // Items are (tile, contraction slice) pairs, slices of a tile adjacent.
   const TileItem it = decode_item(p.plan, blockIdx.x);
   if (it.tile < 0) return;  // uniform per workgroup, before any barrier
@@ -76,7 +79,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdGemmParams p, Codeb
   const int bat = __builtin_amdgcn_readfirstlane(tile_g / p.tiles_per);
   const int tile = tile_g - bat * p.tiles_per;
   const FwdGemmProblem& P = p.prob[bat];
-  const int tm = __builtin_amdgcn_readfirstlane(tile / p.tiles_n), tn = __builtin_amdgcn_readfirstlane(tile % p.tiles_n);
+  const bool n_major = p.tiles_m <= 2;
+  const int tm = __builtin_amdgcn_readfirstlane(n_major ? tile % p.tiles_m : tile / p.tiles_n);
+  const int tn = __builtin_amdgcn_readfirstlane(n_major ? tile / p.tiles_m : tile % p.tiles_n);
 
   codebook_to_lds(lut16, cb, tid);
 
