@@ -178,3 +178,55 @@ def test_storage_round_trip(tmp_path, kind):
     assert rc == -9
     rc = L.qlora_load_4bit(path.encode(), q.QTYPES[kind], N, K // 2, q._p(c2), q._p(q82), q._p(s22), None)
     assert rc == -9
+
+
+def _edge_weights(kind):
+    """Blocks whose weights sit on and next to every edge of a 127- and a
+    128-bin grid over [-1, 1] and every level boundary of the type (a few
+    fp32 ulps and 1e-7 .. 1e-6 either side), under absmax 1 and under a
+    non-power-of-two absmax: the places where an estimate of w / absmax can
+    fall into a neighbouring bin or on the wrong side of a boundary."""
+    xs = []
+    for nb in (127, 128):
+        xs += [-1.0 + b * (2.0 / nb) for b in range(nb + 1)]
+    xs += list(baselines.type_midpoints(kind))
+    vals = []
+    for x in xs:
+        f = np.float32(x)
+        for d in (0, 1, 2, -1, -2):
+            vals.append(np.nextafter(f, np.float32(np.inf if d > 0 else -np.inf)) if d else f)
+            if abs(d) == 2:
+                vals.append(np.nextafter(vals[-1], np.float32(np.inf if d > 0 else -np.inf)))
+        for e in (1e-7, 3e-7, 1e-6, -1e-7, -3e-7, -1e-6):
+            vals.append(np.float32(x + e))
+    vals = np.clip(np.array(vals, dtype=np.float32), -1.0, 1.0)
+    per = 63   # weights per block beside the one that sets absmax
+    nblk = (vals.size + per - 1) // per
+    out = []
+    for scale in (np.float32(1.0), np.float32(0.0371)):
+        w = np.zeros((nblk, 64), dtype=np.float32)
+        w[:, 0] = scale
+        flat = np.zeros(nblk * per, dtype=np.float32)
+        flat[: vals.size] = vals
+        w[:, 1:] = (flat.reshape(nblk, per) * scale).astype(np.float32)
+        out.append(w.ravel())
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("kind", ["nf4", "int4", "fp4"])
+def test_quantize_types_bin_edges_and_boundaries(kind):
+    """Codes of weights on and around every bin edge and level boundary
+    equal the oracle's exact decision, through both quantize kernels."""
+    print(f"bin edges {kind}", flush=True)
+    q = _q()
+    w = _edge_weights(kind)
+    W = _dev_f32(w)
+    codes, absmax = q.quantize_nf4(W, qtype=kind)
+    oc, oa = baselines.quantize_4bit(w, kind)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), oa.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    codes2, q8, s2 = q.quantize_dq(W, kind)
+    oc2, oq8, os2, _ = baselines.quantize_all_4bit(w, kind)
+    assert np.array_equal(codes2.cpu().numpy(), oc2)
+    assert np.array_equal(q8.cpu().numpy(), oq8)
+    assert np.array_equal(s2.cpu().numpy().view(np.uint32), os2.view(np.uint32))
