@@ -9,10 +9,12 @@
 // include/qlora.h.  Every type is quantized by the same rule: the code of the
 // type's level nearest to w/absmax in exact arithmetic.
 //
-// All kernels are HBM-bound streams.  A 64-weight block belongs to 16 lanes
-// (one 16-byte load per lane, a 4-step shuffle max for the absmax); each
-// 16-lane group takes four blocks with their loads issued together.  Codes
-// are decided exactly with fp64 products against the fp64 level boundaries.
+// A 64-weight block belongs to 16 lanes (one vector load per lane, a 4-step
+// DPP row max for the absmax); each 16-lane group takes four blocks with
+// their loads issued together.  Codes are decided exactly with one fp64
+// product and compare per weight against the boundary of the weight's bin.
+// With fp32 sources the kernels run near the HBM stream rate; with bf16
+// sources the per-weight decision work bounds them.
 // The double quantizer gives each group of 256 constants to one wavefront;
 // the fused quantizer gives each group of 256 blocks to one workgroup and
 // keeps the absmax values on chip.
@@ -32,9 +34,8 @@ namespace qlora {
 
 // Each 16-lane group quantizes kQGroupBlocks consecutive blocks; the loads of
 // all of them are issued before any is used, so a wave keeps 4 KiB (fp32) or
-// 2 KiB (bf16) of the weight stream in flight.  The per-weight decision work,
-// not the bytes, bounds these kernels, so bf16 weights keep the same grid
-// (8 blocks per group, half the waves, measured 13 % slower).
+// 2 KiB (bf16) of the weight stream in flight.  bf16 weights keep the same
+// grid (8 blocks per group, half the waves, measured 13 % slower).
 constexpr int kQGroupBlocks = 4;
 
 // Four consecutive weights from e0 as fp32; zero past n.  A bf16 weight
@@ -115,6 +116,7 @@ __device__ __forceinline__ float row16_max(float a) {
   QLORA_ROW_MAX_STEP(a, "row_mirror");
   return a;
 }
+#undef QLORA_ROW_MAX_STEP
 
 // Quantizes the block held by a 16-lane group (lane l16 holds elements
 // 4 l16 .. 4 l16 + 3 in v): returns the 4 codes packed low nibble first and
