@@ -94,3 +94,40 @@ def test_grouped_ragged_against_oracle():
         # XA: fp32 accumulation of K exact bf16 products
         bound = 2 * K * 2.0 ** -24 * (np.abs(X.astype(np.float64)) @ np.abs(A.astype(np.float64))) + 1e-30
         assert np.all(np.abs(XA.cpu().numpy().astype(np.float64) - XAr) <= bound), (N, K)
+
+
+def _random_groups(n, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        count = int(rng.integers(1, 9))
+        T = int(rng.integers(1, 17))
+        r = int(rng.choice([8, 16, 32, 64, 72, 128]))
+        shapes = [(int(rng.integers(1, 260)) * 8, int(rng.integers(1, 34)) * 64) for _ in range(count)]
+        cases.append((shapes, T, r))
+    return cases
+
+
+@pytest.mark.parametrize("shapes,T,r", _random_groups(6))
+def test_grouped_random_against_oracle(shapes, T, r):
+    """Seeded random groups of 1-8 linears with mixed ragged shapes (N up to
+    ~2000, K up to ~2100), T 1-16 and ranks 8-128 in one grouped call: every
+    Y against the oracle, XA within its fp32 accumulation bound."""
+    print(f"grouped random {len(shapes)} linears T={T} r={r}", flush=True)
+    q = _q()
+    alpha = 16.0
+    layers = _make(shapes, T, r, seed0=400 + T + r)
+    outs = q.linear_fwd_grouped(layers, alpha, T, r)
+    torch.cuda.synchronize()
+    for L, (Y, XA) in zip(layers, outs):
+        N, K, seed = L["N"], L["K"], L["seed"]
+        codes, q8, s2, _ = nf4.quantize_all(synth.weight(N, K, seed))
+        Wd = nf4.dequantize(codes, q8, s2, N * K, "bf16").reshape(N, K)
+        X = nf4.bf16_bits_to_f32(synth.x_bits(T, K, seed))
+        A = nf4.bf16_bits_to_f32(synth.a_bits(K, r, seed))
+        B = nf4.bf16_bits_to_f32(synth.b_bits(r, N, seed))
+        Yr, XAr = lora.linear_fwd(X, Wd, A, B, alpha, r)
+        ok, info = compare.check_close(Y.float().cpu().numpy().astype(np.float64), Yr)
+        assert ok, (N, K, info)
+        bound = 2 * K * 2.0 ** -24 * (np.abs(X.astype(np.float64)) @ np.abs(A.astype(np.float64))) + 1e-30
+        assert np.all(np.abs(XA.cpu().numpy().astype(np.float64) - XAr) <= bound), (N, K)
