@@ -20,6 +20,7 @@
 // keeps the absmax values on chip.
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <type_traits>
 
 #include "common.hpp"
@@ -82,13 +83,14 @@ __device__ __forceinline__ uint32_t scan_code(float w, double a64, const Midpoin
 // boundary, none within 1e-5 of a bin edge (checked on the host before the
 // tables are built), so the bin of the fp32 estimate of w / absmax (error
 // below 1e-6) contains its true position or is a neighbour separated from it
-// by no boundary.  Entry b: thr, the bin's boundary (+inf when it has none),
-// and code, the code below it in bits 0..3 and the code above it in bits
-// 4..7; 16 bytes, so one address reaches both.  The host builds them once per
-// launch and passes them by value; each workgroup copies them into LDS.
+// by no boundary.  Entry b is one fp64 word: the bin's boundary (2.0, above
+// every |w| / absmax, when it has none), whose low 8 mantissa bits, zero in
+// every boundary (they have at most 29 significant bits), carry the code
+// below the boundary (bits 0..3) and the code above it (bits 4..7); one 8-byte
+// LDS read per weight gives both.  The host builds the tables once per launch
+// and passes them by value; each workgroup copies them into LDS.
 struct BinEntry {
-  double thr;
-  uint32_t code, pad;
+  uint32_t lo, hi;  // the fp64 word, low dword first
 };
 struct BinTables {
   BinEntry e[kBinsMax];
@@ -139,8 +141,9 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Mi
     for (int i = 0; i < 4; ++i) {
       int b = (int)__builtin_fmaf(v[i], ih, half);
       b = b < nbins - 1 ? b : nbins - 1;
-      const BinEntry& e = bt.e[b];
-      c[i] = (e.code >> (((double)v[i] > a64 * e.thr) ? 4 : 0)) & 15u;
+      const BinEntry e = bt.e[b];
+      const double thr = __hiloint2double((int)e.hi, (int)(e.lo & ~0xFFu));
+      c[i] = (e.lo >> (((double)v[i] > a64 * thr) ? 4 : 0)) & 15u;
     }
   }
   return c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
@@ -411,8 +414,9 @@ bool bins_separate(const Midpoints& mp, int nbins) {
 
 // The bin count for a type: 128, else the nearest count in range that
 // separates its boundaries (INT4's and FP4's fall on edges of 128 bins;
-// 127 separates NF4, INT4 and FP4 alike); 0 when none does, and the
-// launchers then refuse the call (no shipped type comes to that).
+// 127 separates NF4, INT4 and FP4 alike); 0 when none does.  The launchers
+// refuse a call whose type has no bin count or a boundary with low mantissa
+// bits set (no shipped type comes to either).
 int choose_bins(const Midpoints& mp) {
   for (int d = 0; d <= kBinsMax - kBinsMin; ++d) {
     const int lo = 128 - d, hi = 128 + d;
@@ -429,14 +433,17 @@ BinTables make_bins(const Midpoints& mp, int nbins) {
   for (int b = 0; b < nbins; ++b) {
     const double lo = -1.0 + b * (2.0 / nbins), hi = lo + 2.0 / nbins;
     uint32_t cnt = 0;
-    double thr = HUGE_VAL;
+    double thr = 2.0;
     for (int j = 0; j < 15; ++j) {
       if (mp.m[j] < lo) cnt += 1;
       else if (mp.m[j] < hi) thr = mp.m[j];
     }
-    t.e[b].thr = thr;
-    t.e[b].code = level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 4);
-    t.e[b].pad = 0;
+    uint64_t bits;
+    std::memcpy(&bits, &thr, sizeof bits);
+    if (bits & 0xFFu) return BinTables{};  // a boundary using its low mantissa bits: refused (nbins = 0)
+    bits |= level_code(mp, cnt) | (level_code(mp, cnt + 1 < 16 ? cnt + 1 : 15) << 4);
+    t.e[b].lo = (uint32_t)bits;
+    t.e[b].hi = (uint32_t)(bits >> 32);
   }
   return t;
 }
@@ -450,11 +457,11 @@ hipError_t launch_quantize_t(void (*binned_kernel)(const T*, int64_t, uint8_t*, 
   constexpr int G = kQGroupBlocks;
   const int64_t grid = (nb + 16 * G - 1) / (16 * G);
   const int nbins = choose_bins(mp);
-  if (nbins == 0) return hipErrorInvalidValue;
+  const BinTables bins = nbins ? make_bins(mp, nbins) : BinTables{};
+  if (bins.nbins == 0) return hipErrorInvalidValue;
   {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp,
-                       make_bins(mp, nbins));
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, absmax, mp, bins);
   }
   return hipGetLastError();
 }
@@ -467,11 +474,11 @@ hipError_t launch_quantize_dq_t(void (*binned_kernel)(const T*, int64_t, uint8_t
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t grid = (nb + kBlock2 - 1) / kBlock2;
   const int nbins = choose_bins(mp);
-  if (nbins == 0) return hipErrorInvalidValue;
+  const BinTables bins = nbins ? make_bins(mp, nbins) : BinTables{};
+  if (bins.nbins == 0) return hipErrorInvalidValue;
   {
     KernelTimer kt_(name, s);
-    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp,
-                       make_bins(mp, nbins));
+    hipLaunchKernelGGL(binned_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, n, codes, q8, s2, mp, bins);
   }
   return hipGetLastError();
 }
