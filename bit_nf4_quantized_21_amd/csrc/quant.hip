@@ -67,7 +67,11 @@ __device__ __forceinline__ void load_weights4(const uint16_t* __restrict__ W, in
 // kBinsMin and kBinsMax (128 first) whose bins separate the type's
 // boundaries.
 constexpr int kBinsMin = 96, kBinsMax = 160;
-constexpr float kTinyAbsmax = 1e-30f;  // below this, blocks take the exact scan
+// Blocks whose absmax lies outside [kTinyAbsmax, kHugeAbsmax] take the exact
+// scan: there 1/absmax (or its product with nbins/2) would leave the normal
+// fp32 range and the bin estimate would lose its accuracy.
+constexpr float kTinyAbsmax = 1e-30f;
+constexpr float kHugeAbsmax = 0x1p120f;
 
 // Exact scan: level = #{j : w > absmax * m_j} over the type's boundaries
 // (absmax * m_j is exact in fp64; +inf boundaries never count).
@@ -129,7 +133,7 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[4], const Mi
   *amax = a;
   const double a64 = (double)a;
   uint32_t c[4];
-  if (a < kTinyAbsmax) {  // uniform per 16-lane group; absmax 0 -> the zero code
+  if (a < kTinyAbsmax || a > kHugeAbsmax) {  // uniform per 16-lane group; absmax 0 -> the zero code
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = scan_code(v[i], a64, mp);
   } else {

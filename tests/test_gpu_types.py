@@ -29,8 +29,9 @@ def _dev_f32(w):
 
 def _weights(n, seed):
     """N(0, 0.02) weights with an all-zero block, a block of tiny nonzero
-    values (absmax far below 1e-30, including subnormals), and exact ties at
-    the representable level boundaries of every type."""
+    values (absmax far below 1e-30, including subnormals), a block whose
+    absmax is near the top of the fp32 range, and exact ties at the
+    representable level boundaries of every type."""
     w = _rng(seed).normal(0, 0.02, n).astype(np.float32)
     if n >= 64 * 6:
         w[64:128] = 0.0
@@ -38,6 +39,9 @@ def _weights(n, seed):
         w[192:256] = (_rng(seed + 2).normal(0, 1, 64) * 1e-33).astype(np.float32)
         w[256] = 0.5
         w[257:263] = np.float32(0.5) * np.float32([0.0625, 0.125, -0.125, 0.5, 0.25, -0.375])
+    if n >= 64 * 8:
+        w[320:384] = (_rng(seed + 3).normal(0, 1, 64) * 1e37).astype(np.float32)    # absmax near the fp32 top
+        w[320] = np.float32(3.0e38)
     return w
 
 
