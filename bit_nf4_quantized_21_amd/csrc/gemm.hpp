@@ -104,12 +104,16 @@ struct GemvLinear {
   int wg_begin;          // first GEMV workgroup of this linear
   int part_begin;        // first XA-partial workgroup of this linear
 };
-struct GemvGroup {
-  GemvLinear L[kGemvGroupMax];
+// NMAX: the capacity of L.  Launches of a single linear use NMAX = 1, so their
+// kernel argument block is an eighth of the size.
+template <int NMAX>
+struct GemvGroupT {
+  GemvLinear L[NMAX];
   int count;
   int T, r, RP;          // RP = r rounded up to 64
   float s;
 };
+using GemvGroup = GemvGroupT<kGemvGroupMax>;
 hipError_t launch_gemv_group(GemvGroup g, const Codebook& cb, hipStream_t s);
 
 hipError_t launch_gemm_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s);

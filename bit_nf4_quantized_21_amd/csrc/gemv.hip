@@ -54,11 +54,12 @@ constexpr int kXaPitch = kMaxR + 4;  // floats per row of XA / B^T in LDS (16-by
 // (8 / (RP/16))-th 32-k step of each window, starting at w / (RP/16).  A
 // window's rows of A are contiguous, so they are staged with plain 16-byte
 // loads and read back column-wise from LDS.
-__global__ __launch_bounds__(512) void xa_partial_kernel(GemvGroup G) {
+template <int NMAX>
+__global__ __launch_bounds__(512) void xa_partial_kernel(GemvGroupT<NMAX> G) {
   // The linear of this workgroup (uniform: a scalar search over the group).
   int li = 0;
 #pragma unroll
-  for (int j = 1; j < kGemvGroupMax; ++j)
+  for (int j = 1; j < NMAX; ++j)
     if (j < G.count && (int)blockIdx.x >= G.L[j].part_begin) li = j;
   const GemvLinear& Lin = G.L[li];
   const uint16_t* __restrict__ X = Lin.X;
@@ -146,13 +147,13 @@ struct ChunkRegs {
 // groups put more weight bytes in flight per wave (4 KiB per chunk at
 // RG = 4) and share each X load among more rows; the launcher picks RG so
 // the grid still fills the GPU.
-template <int RG>
-__global__ __launch_bounds__(kThreads) void gemv_fwd_kernel(GemvGroup G, Codebook cb) {
+template <int RG, int NMAX>
+__global__ __launch_bounds__(kThreads) void gemv_fwd_kernel(GemvGroupT<NMAX> G, Codebook cb) {
   constexpr int ROWS = 16 * RG;
   static_assert(kWaves * ROWS * 17 * 4 <= kPartLdsBytes, "wave sums fit the partial area");
   int li = 0;
 #pragma unroll
-  for (int j = 1; j < kGemvGroupMax; ++j)
+  for (int j = 1; j < NMAX; ++j)
     if (j < G.count && (int)blockIdx.x >= G.L[j].wg_begin) li = j;
   const GemvLinear& p = G.L[li];
   const int bid = (int)blockIdx.x - p.wg_begin;  // workgroup of this linear
@@ -322,6 +323,26 @@ GemvPlan gemv_plan(int64_t N, int64_t K, int64_t T, int32_t r) {
   return g;
 }
 
+namespace {
+template <int NMAX>
+hipError_t launch_gemv_kernels(const GemvGroupT<NMAX>& g, int parts, int wg, int RG, const Codebook& cb,
+                               hipStream_t s) {
+  {
+    KernelTimer kt_("xa_partial_kernel", s);
+    hipLaunchKernelGGL(xa_partial_kernel<NMAX>, dim3(parts), dim3(512), 0, s, g);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    KernelTimer kt_("gemv_fwd_kernel", s);
+    if (RG == 4) hipLaunchKernelGGL((gemv_fwd_kernel<4, NMAX>), dim3(wg), dim3(kThreads), 0, s, g, cb);
+    else if (RG == 2) hipLaunchKernelGGL((gemv_fwd_kernel<2, NMAX>), dim3(wg), dim3(kThreads), 0, s, g, cb);
+    else hipLaunchKernelGGL((gemv_fwd_kernel<1, NMAX>), dim3(wg), dim3(kThreads), 0, s, g, cb);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemv_group(GemvGroup g, const Codebook& cb, hipStream_t s) {
   // Linears with the longest rows first (a stable sort by K): their
   // workgroups take the longest, so starting them first keeps the last
@@ -352,19 +373,17 @@ hipError_t launch_gemv_group(GemvGroup g, const Codebook& cb, hipStream_t s) {
     wg += (int)((L.N + 16 * RG - 1) / (16 * RG));
     parts += pl.nparts;
   }
-  {
-    KernelTimer kt_("xa_partial_kernel", s);
-    hipLaunchKernelGGL(xa_partial_kernel, dim3(parts), dim3(512), 0, s, g);
+  if (g.count == 1) {
+    GemvGroupT<1> g1{};
+    g1.L[0] = g.L[0];
+    g1.count = 1;
+    g1.T = g.T;
+    g1.r = g.r;
+    g1.RP = g.RP;
+    g1.s = g.s;
+    return launch_gemv_kernels(g1, parts, wg, RG, cb, s);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  {
-    KernelTimer kt_("gemv_fwd_kernel", s);
-    if (RG == 4) hipLaunchKernelGGL(gemv_fwd_kernel<4>, dim3(wg), dim3(kThreads), 0, s, g, cb);
-    else if (RG == 2) hipLaunchKernelGGL(gemv_fwd_kernel<2>, dim3(wg), dim3(kThreads), 0, s, g, cb);
-    else hipLaunchKernelGGL(gemv_fwd_kernel<1>, dim3(wg), dim3(kThreads), 0, s, g, cb);
-  }
-  return hipGetLastError();
+  return launch_gemv_kernels(g, parts, wg, RG, cb, s);
 }
 
 hipError_t launch_gemv_fwd(const FwdGemmParams& p, const Codebook& cb, hipStream_t s) {
